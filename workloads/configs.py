@@ -1,0 +1,140 @@
+"""The attention-forward workloads, as shapes + seeds, and their synthetic inputs.
+
+Each workload stands in for a kind of call the pages describe (video-diffusion
+joint attention, a causal GQA decoder with a relative bias, tabular in-context
+learning in fp16, a D=256 8:1 GQA encoder with padded K/V, and D=256 decode).
+No model, weight or dataset is involved: every input is a seeded draw from
+``workloads.gen``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import gen
+
+
+@dataclasses.dataclass
+class Spec:
+    name: str
+    dtype: str
+    B: int
+    Sq: int              # dense: per-batch query length; varlen: filled with total_q
+    Sk: int              # dense: per-batch key length (padded length when seqused_k); varlen: total_k
+    Hq: int
+    Hkv: int
+    D: int
+    Dv: int
+    causal: bool
+    scale: float         # float32 value used by both sides
+    seed: int
+    # varlen: either explicit lengths or a [lo, hi] range drawn from the seed (q and k share them)
+    varlen: bool = False
+    lengths: Optional[Sequence[int]] = None
+    len_range: Optional[Sequence[int]] = None
+    # padded K/V: seqused_k drawn uniform in [lo, hi] (or explicit)
+    seqused_range: Optional[Sequence[int]] = None
+    seqused: Optional[Sequence[int]] = None
+    rel_extent: int = 0  # E; 0 = no relative bias
+    bias_std: float = 0.5
+    num_splits: int = 1  # <= 0: heuristic
+    pack_gqa: int = -1   # -1 auto, 0 off, 1 on
+    q_std: float = 1.0
+    k_std: float = 1.0
+    v_std: float = 1.0
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+
+def f32(x: float) -> float:
+    return float(np.float32(x))
+
+
+def make_inputs(spec: Spec) -> dict:
+    """Draw the inputs of ``spec`` (uint16 bit patterns for 16-bit tensors, int32 metadata).
+
+    Draw order: lengths (varlen), seqused_k, q, k, v, rel_bias.
+    """
+    rng = gen.make_rng(spec.seed)
+    out: dict = {}
+    if spec.varlen:
+        if spec.lengths is not None:
+            lens = np.asarray(spec.lengths, dtype=np.int32)
+        else:
+            lo, hi = spec.len_range
+            lens = gen.uniform_ints(rng, lo, hi, spec.B)
+        cu = gen.cu_seqlens(lens)
+        out["cu_seqlens_q"] = cu
+        out["cu_seqlens_k"] = cu.copy()
+        out["max_seqlen_q"] = int(lens.max()) if len(lens) else 0
+        out["max_seqlen_k"] = int(lens.max()) if len(lens) else 0
+        Tq = int(cu[-1])
+        Tk = int(cu[-1])
+        spec.Sq = Tq
+        spec.Sk = Tk
+        qshape = (Tq, spec.Hq, spec.D)
+        kshape = (Tk, spec.Hkv, spec.D)
+        vshape = (Tk, spec.Hkv, spec.Dv)
+        nrows_q = Tq
+    else:
+        qshape = (spec.B, spec.Sq, spec.Hq, spec.D)
+        kshape = (spec.B, spec.Sk, spec.Hkv, spec.D)
+        vshape = (spec.B, spec.Sk, spec.Hkv, spec.Dv)
+        nrows_q = spec.B * spec.Sq
+    if spec.seqused is not None:
+        out["seqused_k"] = np.asarray(spec.seqused, dtype=np.int32)
+    elif spec.seqused_range is not None:
+        lo, hi = spec.seqused_range
+        out["seqused_k"] = gen.uniform_ints(rng, lo, hi, spec.B)
+    out["q"] = gen.normal_bits(rng, qshape, spec.dtype, spec.q_std)
+    out["k"] = gen.normal_bits(rng, kshape, spec.dtype, spec.k_std)
+    out["v"] = gen.normal_bits(rng, vshape, spec.dtype, spec.v_std)
+    if spec.rel_extent:
+        out["rel_bias"] = gen.normal_bits(rng, (nrows_q, spec.Hq, spec.rel_extent),
+                                          spec.dtype, spec.bias_std)
+    return out
+
+
+def workload(name: str, dtype: Optional[str] = None) -> Spec:
+    """The named full-size workloads.
+
+    c1   non-causal MHA bf16 [1,257,8,128]                   (small; full oracle)
+    c2   non-causal MHA bf16 [1,20480,56,128] (also fp16)     (video joint attention)
+    c3   varlen causal GQA 32/8 D128, rel_bias E=256, bf16    (8 seqs, len U[512,8192])
+    c4a  fp16 self-attention [256,10000,6,64]
+    c4b  fp16 feature attention [100,100000,4,16]
+    c4c  fp16 cross attention q[1,1000,6,64] k/v[1,1e6,6,64], split-KV heuristic
+    c5a  bf16 D256 8:1 pack-GQA, q[4,1024,8,256], k/v[4,2048,1,256], seqused_k U[600,2048]
+    c5b  bf16 D256 decode q[32,1,8,256], k/v[32,131072,1,256], causal, split-KV + combine
+    """
+    s128 = f32(1.0 / math.sqrt(128.0))
+    if name == "c1":
+        return Spec(name, dtype or gen.BF16, 1, 257, 257, 8, 8, 128, 128, False, s128, 1)
+    if name == "c2":
+        return Spec(name, dtype or gen.BF16, 1, 20480, 20480, 56, 56, 128, 128, False, s128, 2)
+    if name == "c3":
+        return Spec(name, dtype or gen.BF16, 8, 0, 0, 32, 8, 128, 128, True, s128, 3,
+                    varlen=True, len_range=(512, 8192), rel_extent=256, bias_std=0.5)
+    if name == "c4a":
+        return Spec(name, dtype or gen.FP16, 256, 10000, 10000, 6, 6, 64, 64, False, f32(1 / 8), 41)
+    if name == "c4b":
+        return Spec(name, dtype or gen.FP16, 100, 100000, 100000, 4, 4, 16, 16, False, f32(1 / 4), 42)
+    if name == "c4c":
+        return Spec(name, dtype or gen.FP16, 1, 1000, 1000000, 6, 6, 64, 64, False, f32(1 / 8), 43,
+                    num_splits=0)
+    if name == "c5a":
+        return Spec(name, dtype or gen.BF16, 4, 1024, 2048, 8, 1, 256, 256, False, f32(1 / 16), 51,
+                    seqused_range=(600, 2048), pack_gqa=1)
+    if name == "c5b":
+        return Spec(name, dtype or gen.BF16, 32, 1, 131072, 8, 1, 256, 256, True, f32(1 / 16), 52,
+                    num_splits=0, pack_gqa=1)
+    raise KeyError(name)
+
+
+WORKLOADS = ("c1", "c2", "c3", "c4a", "c4b", "c4c", "c5a", "c5b")
+
