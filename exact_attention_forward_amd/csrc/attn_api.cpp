@@ -1,0 +1,308 @@
+// attn_api.cpp -- the C ABI: argument validation, planning and kernel dispatch.
+//
+// The host side stays short on purpose: one validation pass, a few integer
+// divisions to size the grid, one launch (plus the combine launch when the key
+// range is split). Per-call host overhead is what remains visible for short
+// calls (TabPFN issue #1235, last comment), so nothing here allocates,
+// synchronises or reads device memory.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/attn.h"
+#include "kernels.h"
+
+using namespace mi355attn;
+
+namespace {
+
+constexpr int kNumCUs = 256;  // MI355X compute units
+
+bool is_aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool head_dim_ok(int D) { return D == 16 || D == 64 || D == 128 || D == 256; }
+
+// product of non-negative ints, false if it reaches 2^62
+bool mul_ok(long long& acc, long long x) {
+    if (x < 0) return false;
+    if (x == 0 || acc == 0) {
+        acc = 0;
+        return true;
+    }
+    if (acc > (1LL << 62) / x) return false;
+    acc *= x;
+    return true;
+}
+
+struct Plan {
+    bool varlen;
+    int G, gp, n_hg, n_tiles, ns, nkb_max;
+    long long rows_q;
+    long long nblocks;
+};
+
+// Tile geometry shared with the kernels; returns false for sizes that cannot be planned.
+bool make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int is_varlen, int max_seqlen_q,
+               int max_seqlen_k, int pack_gqa, int num_splits, Plan& pl) {
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || !head_dim_ok(D)) return false;
+    pl.varlen = is_varlen != 0;
+    pl.G = Hq / Hkv;
+    const bool pack = pack_gqa == 1 || (pack_gqa == -1 && pl.G > 1);
+    pl.gp = pack ? pl.G : 1;
+    pl.n_hg = pack ? Hkv : Hq;
+    const long long qmax = pl.varlen ? max_seqlen_q : Sq;
+    const long long kmax = pl.varlen ? max_seqlen_k : Sk;
+    const int bm = tile_bm(D), bn = tile_bn(D);
+    const long long nt = (qmax * pl.gp + bm - 1) / bm;
+    if (nt > INT32_MAX) return false;
+    pl.n_tiles = (int)nt;
+    pl.nkb_max = (int)((kmax + bn - 1) / bn);
+    pl.rows_q = pl.varlen ? (long long)Sq : (long long)B * Sq;
+    const long long base = (long long)B * pl.n_hg * pl.n_tiles;
+    int ns;
+    if (pl.nkb_max <= 1) {
+        ns = 1;
+    } else if (num_splits >= 1) {
+        ns = num_splits;
+        if (ns > pl.nkb_max) ns = pl.nkb_max;
+        if (ns > ATTN_MAX_SPLITS) ns = ATTN_MAX_SPLITS;
+    } else if (base == 0 || base >= kNumCUs) {
+        ns = 1;
+    } else {
+        ns = (int)(kNumCUs / base);
+        const int cap = pl.nkb_max / 4 > 0 ? pl.nkb_max / 4 : 1;
+        if (ns > cap) ns = cap;
+        if (ns > ATTN_MAX_SPLITS) ns = ATTN_MAX_SPLITS;
+        if (ns < 1) ns = 1;
+    }
+    pl.ns = ns;
+    pl.nblocks = base * ns;
+    return true;
+}
+
+size_t workspace_bytes_for(long long rows_q, int Hq, int Dv, int ns) {
+    if (ns <= 1) return 0;
+    return (size_t)ns * (size_t)rows_q * (size_t)Hq * ((size_t)Dv + 1) * sizeof(float);
+}
+
+attn_status_t validate(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                       int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale,
+                       const int* cu_q, const int* cu_k, int max_seqlen_q, int max_seqlen_k,
+                       const void* rel_bias, int rel_extent, int num_splits, int pack_gqa,
+                       attn_dtype_t dtype, void* workspace, size_t workspace_bytes, Plan& pl) {
+    if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_BAD_DTYPE;
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Dv <= 0) return ATTN_ERR_BAD_SHAPE;
+    if (D != Dv || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+    if (Hq % Hkv) return ATTN_ERR_BAD_GQA;
+    if (!isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+    if (pack_gqa < -1 || pack_gqa > 1) return ATTN_ERR_BAD_ARG;
+    if ((cu_q == nullptr) != (cu_k == nullptr)) return ATTN_ERR_BAD_VARLEN;
+    const bool varlen = cu_q != nullptr;
+    if (varlen) {
+        if (max_seqlen_q < 0 || max_seqlen_k < 0 || max_seqlen_q > Sq || max_seqlen_k > Sk)
+            return ATTN_ERR_BAD_VARLEN;
+        if (B > 0 && Sq > 0 && max_seqlen_q == 0) return ATTN_ERR_BAD_VARLEN;
+        if (B > 0 && Sk > 0 && max_seqlen_k == 0) return ATTN_ERR_BAD_VARLEN;
+    }
+    // element counts below 2^62
+    long long nq = 1, nk = 1;
+    if (!mul_ok(nq, varlen ? 1 : B) || !mul_ok(nq, Sq) || !mul_ok(nq, Hq) || !mul_ok(nq, D))
+        return ATTN_ERR_BAD_SHAPE;
+    if (!mul_ok(nk, varlen ? 1 : B) || !mul_ok(nk, Sk) || !mul_ok(nk, Hkv) || !mul_ok(nk, D))
+        return ATTN_ERR_BAD_SHAPE;
+    if (rel_bias) {
+        if (rel_extent <= 0 || rel_extent % 128) return ATTN_ERR_BAD_REL_EXTENT;
+        long long nb = 1;
+        if (!mul_ok(nb, varlen ? 1 : B) || !mul_ok(nb, Sq) || !mul_ok(nb, Hq) || !mul_ok(nb, rel_extent))
+            return ATTN_ERR_BAD_SHAPE;
+    } else if (rel_extent != 0) {
+        return ATTN_ERR_BAD_REL_EXTENT;
+    }
+    if (!make_plan(B, Sq, Sk, Hq, Hkv, D, varlen, max_seqlen_q, max_seqlen_k, pack_gqa, num_splits, pl))
+        return ATTN_ERR_BAD_SHAPE;
+    if (pl.nblocks > INT32_MAX) return ATTN_ERR_BAD_SHAPE;
+    const bool has_rows = pl.rows_q > 0 && B > 0;
+    if (has_rows && (!q || !out)) return ATTN_ERR_NULL_POINTER;
+    if (has_rows && Sk > 0 && (!k || !v)) return ATTN_ERR_NULL_POINTER;
+    if (!is_aligned(q, 16) || !is_aligned(k, 16) || !is_aligned(v, 16) || !is_aligned(out, 16) ||
+        !is_aligned(lse, 4) || !is_aligned(rel_bias, 2) || !is_aligned(workspace, 16))
+        return ATTN_ERR_MISALIGNED;
+    if (pl.ns > 1) {
+        if (!workspace) return ATTN_ERR_WORKSPACE;
+        if (workspace_bytes < workspace_bytes_for(pl.rows_q, Hq, Dv, pl.ns)) return ATTN_ERR_WORKSPACE;
+    }
+    return ATTN_OK;
+}
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* e = getenv("ATTN_LOG");
+        return e && e[0] && e[0] != '0';
+    }();
+    return on;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_check_args(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale,
+                              int causal, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                              int max_seqlen_q, int max_seqlen_k, const int* seqused_k,
+                              const void* rel_bias, int rel_extent, int num_splits, int pack_gqa,
+                              attn_dtype_t dtype, void* workspace, size_t workspace_bytes) {
+    (void)causal;
+    (void)seqused_k;
+    Plan pl;
+    return validate(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, Dv, scale, cu_seqlens_q, cu_seqlens_k,
+                    max_seqlen_q, max_seqlen_k, rel_bias, rel_extent, num_splits, pack_gqa, dtype,
+                    workspace, workspace_bytes, pl);
+}
+
+int attn_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_varlen,
+                    int max_seqlen_q, int max_seqlen_k, int pack_gqa, int num_splits) {
+    if (D != Dv) return 0;
+    Plan pl;
+    if (!make_plan(B, Sq, Sk, Hq, Hkv, D, is_varlen, max_seqlen_q, max_seqlen_k, pack_gqa, num_splits, pl))
+        return 0;
+    return pl.ns;
+}
+
+size_t attn_fwd_workspace_size(int B, int Sq, int Hq, int Dv, int is_varlen, int num_splits) {
+    if (B < 0 || Sq < 0 || Hq <= 0 || Dv <= 0) return 0;
+    const long long rows_q = is_varlen ? (long long)Sq : (long long)B * Sq;
+    return workspace_bytes_for(rows_q, Hq, Dv, num_splits);
+}
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                       int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale, int causal,
+                       const int* cu_seqlens_q, const int* cu_seqlens_k, int max_seqlen_q,
+                       int max_seqlen_k, const int* seqused_k, const void* rel_bias, int rel_extent,
+                       int num_splits, int pack_gqa, attn_dtype_t dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    Plan pl;
+    const attn_status_t st =
+        validate(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, Dv, scale, cu_seqlens_q, cu_seqlens_k,
+                 max_seqlen_q, max_seqlen_k, rel_bias, rel_extent, num_splits, pack_gqa, dtype,
+                 workspace, workspace_bytes, pl);
+    if (st != ATTN_OK) return st;
+    if (pl.nblocks == 0) return ATTN_OK;  // no rows to compute
+
+    FwdParams p;
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.out = (uint16_t*)out;
+    p.lse = lse;
+    p.bias = (const uint16_t*)rel_bias;
+    p.o_part = nullptr;
+    p.lse_part = nullptr;
+    if (pl.ns > 1) {
+        p.o_part = (float*)workspace;
+        p.lse_part = p.o_part + (size_t)pl.ns * (size_t)pl.rows_q * (size_t)Hq * (size_t)Dv;
+    }
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.seqused_k = seqused_k;
+    p.B = B;
+    p.Sq = Sq;
+    p.Sk = Sk;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.G = pl.G;
+    p.gp = pl.gp;
+    p.n_hg = pl.n_hg;
+    p.n_tiles = pl.n_tiles;
+    p.ns = pl.ns;
+    p.E = rel_bias ? rel_extent : 0;
+    p.nblocks = (int)pl.nblocks;
+    p.c2 = scale * 1.4426950408889634f;
+    p.rows_q = pl.rows_q;
+
+    const bool bf = dtype == ATTN_BF16;
+    const bool split = pl.ns > 1;
+    hipStream_t s = (hipStream_t)stream;
+    if (log_enabled())
+        fprintf(stderr, "[attn] D=%d %s causal=%d varlen=%d bias=%d gp=%d n_hg=%d tiles=%d splits=%d grid=%lld\n",
+                D, bf ? "bf16" : "fp16", causal ? 1 : 0, pl.varlen ? 1 : 0, rel_bias ? 1 : 0, pl.gp, pl.n_hg,
+                pl.n_tiles, pl.ns, pl.nblocks);
+    hipError_t e;
+    switch (D) {
+        case 16: e = launch_fwd_d16(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, s); break;
+        case 64: e = launch_fwd_d64(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, s); break;
+        case 128: e = launch_fwd_d128(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, s); break;
+        case 256: e = launch_fwd_d256(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, s); break;
+        default: return ATTN_ERR_UNSUPPORTED_COMBO;
+    }
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+    if (split) {
+        CombineParams c;
+        c.o_part = p.o_part;
+        c.lse_part = p.lse_part;
+        c.out = p.out;
+        c.lse = lse;
+        c.rows_q = pl.rows_q;
+        c.Hq = Hq;
+        c.Sq = Sq;
+        c.ns = pl.ns;
+        c.is_varlen = pl.varlen ? 1 : 0;
+        if (launch_combine(c, Dv, bf, s) != hipSuccess) return ATTN_ERR_HIP;
+    }
+    return ATTN_OK;
+}
+
+attn_status_t attn_combine(const float* o_partial, const float* lse_partial, int num_splits, void* out,
+                           float* lse, int B, int Sq, int Hq, int Dv, int is_varlen, attn_dtype_t dtype,
+                           void* stream) {
+    if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_BAD_DTYPE;
+    if (B < 0 || Sq < 0 || Hq <= 0) return ATTN_ERR_BAD_SHAPE;
+    if (!head_dim_ok(Dv)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+    if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_BAD_SPLITS;
+    const long long rows_q = is_varlen ? (long long)Sq : (long long)B * Sq;
+    long long n = rows_q;
+    if (!mul_ok(n, Hq) || !mul_ok(n, Dv) || !mul_ok(n, num_splits)) return ATTN_ERR_BAD_SHAPE;
+    if (rows_q == 0) return ATTN_OK;
+    if (!o_partial || !lse_partial || !out) return ATTN_ERR_NULL_POINTER;
+    if (!is_aligned(o_partial, 16) || !is_aligned(lse_partial, 4) || !is_aligned(out, 16) || !is_aligned(lse, 4))
+        return ATTN_ERR_MISALIGNED;
+    if ((rows_q * Hq + 3) / 4 > INT32_MAX) return ATTN_ERR_BAD_SHAPE;
+    CombineParams c;
+    c.o_part = o_partial;
+    c.lse_part = lse_partial;
+    c.out = (uint16_t*)out;
+    c.lse = lse;
+    c.rows_q = rows_q;
+    c.Hq = Hq;
+    c.Sq = Sq;
+    c.ns = num_splits;
+    c.is_varlen = is_varlen ? 1 : 0;
+    return launch_combine(c, Dv, dtype == ATTN_BF16, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+const char* attn_status_string(attn_status_t s) {
+    switch (s) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case ATTN_ERR_BAD_SHAPE: return "invalid or overflowing sizes";
+        case ATTN_ERR_BAD_DTYPE: return "dtype must be bf16 or fp16";
+        case ATTN_ERR_UNSUPPORTED_HEAD_DIM: return "head dim must satisfy D == Dv in {16, 64, 128, 256}";
+        case ATTN_ERR_BAD_GQA: return "Hq must be a multiple of Hkv";
+        case ATTN_ERR_BAD_REL_EXTENT: return "rel_extent must be a positive multiple of 128 and needs rel_bias";
+        case ATTN_ERR_BAD_VARLEN: return "cu_seqlens_q/k must be given together with valid max_seqlen";
+        case ATTN_ERR_MISALIGNED: return "pointer misaligned (q/k/v/out/workspace 16 B, lse 4 B, rel_bias 2 B)";
+        case ATTN_ERR_WORKSPACE: return "split-KV needs a workspace of attn_fwd_workspace_size bytes";
+        case ATTN_ERR_UNSUPPORTED_COMBO: return "no kernel for this combination";
+        case ATTN_ERR_HIP: return "HIP runtime error at launch";
+        case ATTN_ERR_BAD_SPLITS: return "num_splits must be in [1, 256]";
+        case ATTN_ERR_BAD_SCALE: return "scale must be finite";
+        case ATTN_ERR_BAD_ARG: return "pack_gqa must be -1, 0 or 1";
+    }
+    return "unknown status";
+}
+
+const char* attn_version(void) { return "mi355-attn 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,11 @@
+// Forward-kernel instances for head dim 128 (bf16/fp16 x causal x varlen x bias x split).
+#include "fwd_kernel.hpp"
+
+namespace mi355attn {
+
+hipError_t launch_fwd_d128(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
+                          bool split, hipStream_t s) {
+    return launch_fwd_any<128>(p, bf16, causal, varlen, bias, split, s);
+}
+
+}  // namespace mi355attn

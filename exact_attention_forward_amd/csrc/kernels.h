@@ -1,0 +1,64 @@
+// kernels.h -- parameters and launchers shared by the host planner and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355attn {
+
+// Work-group geometry of the forward kernel for head dim D (D == Dv).
+//   4 waves of 64 lanes; each wave owns NQB blocks of 32 query rows
+//   (one MFMA 32x32 output column block per row block); BN keys per K/V tile.
+struct TileGeom {
+    int nqb;   // 32-row blocks per wave
+    int bm;    // rows per work-group = 4 * 32 * nqb
+    int bn;    // keys per K/V tile
+};
+
+__host__ __device__ constexpr int tile_nqb(int D) { return D <= 128 ? 2 : 1; }
+__host__ __device__ constexpr int tile_bm(int D) { return 4 * 32 * tile_nqb(D); }
+__host__ __device__ constexpr int tile_bn(int /*D*/) { return 64; }
+
+struct FwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* out;
+    float* lse;            // may be null
+    const uint16_t* bias;  // rel_bias or null
+    float* o_part;         // split partials (split mode)
+    float* lse_part;
+    const int* cu_q;       // varlen offsets (varlen mode)
+    const int* cu_k;
+    const int* seqused_k;  // may be null
+    int B, Sq, Sk, Hq, Hkv;
+    int G;                 // Hq / Hkv
+    int gp;                // query heads packed per tile row group (G with pack-GQA, else 1)
+    int n_hg;              // head groups: Hkv when packed, else Hq
+    int n_tiles;           // row tiles per (batch, head group)
+    int ns;                // key-range splits (1 = none)
+    int E;                 // rel_extent (0 without bias)
+    int nblocks;           // grid size
+    float c2;              // scale * log2(e)
+    long long rows_q;      // rows of q's flattened order: B*Sq (dense) or total_q (varlen)
+};
+
+struct CombineParams {
+    const float* o_part;
+    const float* lse_part;
+    uint16_t* out;
+    float* lse;            // may be null
+    long long rows_q;      // rows of q's flattened order
+    int Hq, Sq, ns, is_varlen;
+};
+
+hipError_t launch_fwd_d16(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
+                          bool split, hipStream_t s);
+hipError_t launch_fwd_d64(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
+                          bool split, hipStream_t s);
+hipError_t launch_fwd_d128(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
+                           bool split, hipStream_t s);
+hipError_t launch_fwd_d256(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
+                           bool split, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, int Dv, bool bf16, hipStream_t s);
+
+}  // namespace mi355attn

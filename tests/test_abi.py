@@ -1,0 +1,142 @@
+"""The C-ABI library loads on the CPU, exports every declared symbol, and validates arguments.
+
+No GPU call is made here: attn_check_args, attn_num_splits, attn_fwd_workspace_size,
+attn_status_string and attn_version are pure host functions. Pointers are fake
+addresses that are only checked for NULL and alignment.
+"""
+import os
+import re
+
+import pytest
+
+import exact_attention_forward_amd as fa
+from exact_attention_forward_amd import CODE
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 0x10000  # a fake, 16-byte aligned device address
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        from exact_attention_forward_amd import build
+        build.build()
+    return fa.load()
+
+
+def declared_functions():
+    with open(os.path.join(REPO, "include", "attn.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(attn_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(fa.SIGNATURES), (names, sorted(fa.SIGNATURES))
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+
+
+def test_version_and_status_strings(lib):
+    assert "gfx950" in fa.version()
+    for code in range(0, 15):
+        s = fa.status_string(code)
+        assert s and s != "unknown status"
+    assert fa.status_string(99) == "unknown status"
+
+
+def args(**over):
+    a = dict(q=A, k=A, v=A, out=A, lse=A, B=1, Sq=257, Sk=257, Hq=8, Hkv=8, D=128, Dv=128,
+             scale=0.0883883, causal=0, cu_q=None, cu_k=None, max_q=0, max_k=0, seqused=None,
+             bias=None, E=0, ns=1, pack=-1, dtype=0, ws=None, ws_bytes=0)
+    a.update(over)
+    return a
+
+
+def check(lib, **over):
+    a = args(**over)
+    return lib.attn_check_args(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Sq"], a["Sk"],
+                               a["Hq"], a["Hkv"], a["D"], a["Dv"], a["scale"], a["causal"], a["cu_q"],
+                               a["cu_k"], a["max_q"], a["max_k"], a["seqused"], a["bias"], a["E"],
+                               a["ns"], a["pack"], a["dtype"], a["ws"], a["ws_bytes"])
+
+
+def test_valid_calls(lib):
+    assert check(lib) == 0
+    for D in (16, 64, 128, 256):
+        assert check(lib, D=D, Dv=D) == 0
+    assert check(lib, dtype=1) == 0
+    assert check(lib, Hq=32, Hkv=8, causal=1) == 0
+    assert check(lib, cu_q=A, cu_k=A, max_q=100, max_k=100, B=3, Sq=257, Sk=257) == 0
+    assert check(lib, bias=A, E=256) == 0
+    assert check(lib, lse=None) == 0
+    assert check(lib, seqused=A) == 0
+    # nothing to compute: NULL tensors are fine
+    assert check(lib, B=0, q=None, k=None, v=None, out=None) == 0
+    assert check(lib, Sk=0, k=None, v=None) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=2), "ATTN_ERR_BAD_DTYPE"),
+    (dict(B=-1), "ATTN_ERR_BAD_SHAPE"),
+    (dict(Sq=-3), "ATTN_ERR_BAD_SHAPE"),
+    (dict(Hq=0), "ATTN_ERR_BAD_SHAPE"),
+    (dict(D=96, Dv=96), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(D=128, Dv=64), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(D=512, Dv=512), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(Hq=8, Hkv=3), "ATTN_ERR_BAD_GQA"),
+    (dict(bias=A, E=100), "ATTN_ERR_BAD_REL_EXTENT"),
+    (dict(bias=A, E=0), "ATTN_ERR_BAD_REL_EXTENT"),
+    (dict(bias=None, E=128), "ATTN_ERR_BAD_REL_EXTENT"),
+    (dict(cu_q=A), "ATTN_ERR_BAD_VARLEN"),
+    (dict(cu_k=A), "ATTN_ERR_BAD_VARLEN"),
+    (dict(cu_q=A, cu_k=A, max_q=0, max_k=10), "ATTN_ERR_BAD_VARLEN"),
+    (dict(cu_q=A, cu_k=A, max_q=300, max_k=10), "ATTN_ERR_BAD_VARLEN"),
+    (dict(q=None), "ATTN_ERR_NULL_POINTER"),
+    (dict(out=None), "ATTN_ERR_NULL_POINTER"),
+    (dict(k=None), "ATTN_ERR_NULL_POINTER"),
+    (dict(q=A + 8), "ATTN_ERR_MISALIGNED"),
+    (dict(v=A + 2), "ATTN_ERR_MISALIGNED"),
+    (dict(lse=A + 2), "ATTN_ERR_MISALIGNED"),
+    (dict(bias=A + 1, E=128), "ATTN_ERR_MISALIGNED"),
+    (dict(ns=4, Sk=100000, ws=None), "ATTN_ERR_WORKSPACE"),
+    (dict(ns=4, Sk=100000, ws=A, ws_bytes=16), "ATTN_ERR_WORKSPACE"),
+    (dict(scale=float("nan")), "ATTN_ERR_BAD_SCALE"),
+    (dict(scale=float("inf")), "ATTN_ERR_BAD_SCALE"),
+    (dict(pack=2), "ATTN_ERR_BAD_ARG"),
+    (dict(B=1 << 30, Sq=1 << 30, Hq=1 << 20), "ATTN_ERR_BAD_SHAPE"),
+])
+def test_invalid_calls(lib, over, code):
+    assert check(lib, **over) == CODE[code]
+
+
+def test_workspace_and_splits(lib):
+    # split with a large enough workspace is accepted
+    ns = lib.attn_num_splits(1, 257, 100000, 8, 8, 128, 128, 0, 0, 0, -1, 4)
+    assert ns == 4
+    need = lib.attn_fwd_workspace_size(1, 257, 8, 128, 0, 4)
+    assert need == 4 * 257 * 8 * 129 * 4
+    assert check(lib, ns=4, Sk=100000, ws=A, ws_bytes=need) == 0
+    assert check(lib, ns=4, Sk=100000, ws=A + 4, ws_bytes=need) == CODE["ATTN_ERR_MISALIGNED"]
+    assert lib.attn_fwd_workspace_size(1, 257, 8, 128, 0, 1) == 0
+    # requested splits are clamped to the number of 64-key blocks and to 256
+    assert lib.attn_num_splits(1, 10, 200, 1, 1, 64, 64, 0, 0, 0, -1, 50) == 4
+    assert lib.attn_num_splits(1, 10, 10**6, 1, 1, 64, 64, 0, 0, 0, -1, 1000) == 256
+    # heuristic: no split when the grid already covers the 256 compute units
+    assert lib.attn_num_splits(1, 20480, 20480, 56, 56, 128, 128, 0, 0, 0, -1, 0) == 1
+    # decode B=32, one KV head, 8:1 packed: 32 work-groups -> 8 splits
+    assert lib.attn_num_splits(32, 1, 131072, 8, 1, 256, 256, 0, 0, 0, -1, 0) == 8
+    # short query, long keys: 24 work-groups -> 10 splits
+    assert lib.attn_num_splits(1, 1000, 10**6, 6, 6, 64, 64, 0, 0, 0, -1, 0) == 10
+    # never fewer than 4 key blocks per split
+    assert lib.attn_num_splits(1, 1, 640, 1, 1, 64, 64, 0, 0, 0, -1, 0) == 2
+    # varlen sizes come from max_seqlen
+    assert lib.attn_num_splits(4, 400, 400000, 8, 8, 128, 128, 1, 100, 100000, -1, 0) == 8
+
+
+def test_python_binding_rejects_bad_dtype():
+    import torch
+    x = torch.zeros((1, 4, 1, 64), dtype=torch.float32)
+    with pytest.raises(fa.AttnError):
+        fa.attn_fwd(x, x, x)

@@ -14,6 +14,18 @@ def test_chunked_equals_one_shot():
     assert np.array_equal(c, d)
 
 
+def test_block_streams_independent_of_threads():
+    a = gen.stream_normal_bits(9, gen.STREAM_K, (3 * gen.BLOCK + 12345,), "bf16", threads=1)
+    b = gen.stream_normal_bits(9, gen.STREAM_K, (3 * gen.BLOCK + 12345,), "bf16", threads=5)
+    assert np.array_equal(a, b)
+    # block n is its own stream
+    first = gen.make_rng(9, gen.STREAM_K, 1).standard_normal(10, dtype=np.float32)
+    assert np.array_equal(a[gen.BLOCK:gen.BLOCK + 10], gen.f32_to_bf16_bits(first))
+    # different streams differ
+    c = gen.stream_normal_bits(9, gen.STREAM_V, (1000,), "bf16")
+    assert not np.array_equal(a[:1000], c)
+
+
 def test_bf16_rounding_matches_torch():
     rng = gen.make_rng(3)
     x = np.concatenate([

@@ -58,9 +58,10 @@ def f32(x: float) -> float:
 def make_inputs(spec: Spec) -> dict:
     """Draw the inputs of ``spec`` (uint16 bit patterns for 16-bit tensors, int32 metadata).
 
-    Draw order: lengths (varlen), seqused_k, q, k, v, rel_bias.
+    Integer metadata comes from stream 0 (lengths, then seqused_k); q, k, v and
+    rel_bias from streams 1-4 (see workloads.gen).
     """
-    rng = gen.make_rng(spec.seed)
+    rng = gen.make_rng(spec.seed, gen.STREAM_META)
     out: dict = {}
     if spec.varlen:
         if spec.lengths is not None:
@@ -91,12 +92,13 @@ def make_inputs(spec: Spec) -> dict:
     elif spec.seqused_range is not None:
         lo, hi = spec.seqused_range
         out["seqused_k"] = gen.uniform_ints(rng, lo, hi, spec.B)
-    out["q"] = gen.normal_bits(rng, qshape, spec.dtype, spec.q_std)
-    out["k"] = gen.normal_bits(rng, kshape, spec.dtype, spec.k_std)
-    out["v"] = gen.normal_bits(rng, vshape, spec.dtype, spec.v_std)
+    out["q"] = gen.stream_normal_bits(spec.seed, gen.STREAM_Q, qshape, spec.dtype, spec.q_std)
+    out["k"] = gen.stream_normal_bits(spec.seed, gen.STREAM_K, kshape, spec.dtype, spec.k_std)
+    out["v"] = gen.stream_normal_bits(spec.seed, gen.STREAM_V, vshape, spec.dtype, spec.v_std)
     if spec.rel_extent:
-        out["rel_bias"] = gen.normal_bits(rng, (nrows_q, spec.Hq, spec.rel_extent),
-                                          spec.dtype, spec.bias_std)
+        out["rel_bias"] = gen.stream_normal_bits(spec.seed, gen.STREAM_BIAS,
+                                                 (nrows_q, spec.Hq, spec.rel_extent),
+                                                 spec.dtype, spec.bias_std)
     return out
 
 

@@ -5,15 +5,18 @@ attention forward consumes. It holds none of the attention arithmetic: no dot
 products, masks, softmax or bias rule. Both sides read the exact 16-bit values
 produced here, so they see identical inputs.
 
-Recipe (every tensor):
-  * generator: numpy PCG64 seeded with the workload's seed;
-  * draw order: integer metadata first (sequence lengths, seqused_k), then q, k,
-    v, rel_bias, each drawn in full before the next;
-  * values: float32 standard normal draws, taken in fixed-size chunks so that the
-    stream is independent of the chunk size, multiplied by the tensor's
-    standard deviation in float32, then rounded to nearest-even into bfloat16 or
-    float16;
-  * integer ranges "uniform in [lo, hi]" include both ends.
+Recipe:
+  * every workload has a seed; each tensor has a stream number (0 = integer
+    metadata such as sequence lengths and seqused_k, 1 = q, 2 = k, 3 = v,
+    4 = rel_bias);
+  * a tensor is cut into fixed blocks of 2^22 elements (row-major order); block
+    n is drawn from its own numpy PCG64 generator seeded with
+    SeedSequence([seed, stream, n]), so blocks can be drawn in parallel and the
+    values do not depend on the thread count;
+  * values: float32 standard normal draws, multiplied by the tensor's standard
+    deviation in float32, then rounded to nearest-even into bfloat16 or float16;
+  * integer ranges "uniform in [lo, hi]" include both ends (stream 0, drawn in
+    the order: sequence lengths, then seqused_k).
 """
 from __future__ import annotations
 
@@ -23,12 +26,18 @@ BF16 = "bf16"
 FP16 = "fp16"
 DTYPES = (BF16, FP16)
 
-_CHUNK = 1 << 22  # float32 draws per chunk
+_CHUNK = 1 << 22  # float32 draws per chunk of the sequential helper
+BLOCK = 1 << 22   # elements per independently seeded block of a workload tensor
+
+STREAM_META, STREAM_Q, STREAM_K, STREAM_V, STREAM_BIAS = 0, 1, 2, 3, 4
 
 
-def make_rng(seed: int) -> np.random.Generator:
-    """PCG64 generator for one workload seed."""
-    return np.random.Generator(np.random.PCG64(int(seed)))
+def make_rng(seed: int, stream: int = None, block: int = None) -> np.random.Generator:
+    """PCG64 generator: plain seed, or SeedSequence([seed, stream(, block)])."""
+    if stream is None:
+        return np.random.Generator(np.random.PCG64(int(seed)))
+    key = [int(seed), int(stream)] + ([] if block is None else [int(block)])
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(key)))
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -38,13 +47,16 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     bfloat16 become infinity, as IEEE round-to-nearest-even prescribes.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    r += u            # no overflow: only NaN patterns reach the top of the range
+    r >>= 16
+    out = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        r[nan] = 0x7FC0
-    return r
+        out[nan] = 0x7FC0
+    return out
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -108,6 +120,34 @@ def normal_bits(rng: np.random.Generator, shape, dtype: str, std: float = 1.0,
             b *= s
         out[pos:pos + m] = to_bits(b, dtype)
         pos += m
+    return out.reshape(shape)
+
+
+def stream_normal_bits(seed: int, stream: int, shape, dtype: str, std: float = 1.0,
+                       threads: int = None) -> np.ndarray:
+    """A workload tensor: N(0, std^2) in float32 per independently seeded block, rounded to dtype."""
+    import concurrent.futures
+    import os
+    n = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(n, dtype=np.uint16)
+    nblocks = (n + BLOCK - 1) // BLOCK
+    s = np.float32(std)
+
+    def fill(bi):
+        lo = bi * BLOCK
+        m = min(BLOCK, n - lo)
+        x = make_rng(seed, stream, bi).standard_normal(m, dtype=np.float32)
+        if std != 1.0:
+            x *= s
+        out[lo:lo + m] = to_bits(x, dtype)
+
+    workers = threads or min(16, os.cpu_count() or 1)
+    if workers <= 1 or nblocks <= 1:
+        for bi in range(nblocks):
+            fill(bi)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, range(nblocks)))
     return out.reshape(shape)
 
 
