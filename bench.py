@@ -1,0 +1,316 @@
+"""Benchmark of the MI355X exact attention forward (one JSON line on stdout).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--dtype bf16]
+
+A step is one full forward call (attn_fwd: the fused kernel, plus the combine
+kernel when the key range is split) over one batch of synthetic inputs that is
+already resident in HBM. The default workload is the non-causal MHA forward
+q/k/v [1, 20480, 56, 128] in bf16 (video joint-attention shape).
+
+Reported:
+  value       whole-job TFLOP/s (GB/s for the decode workload) over the K timed steps
+  roofline    achieved / peak of the dominant kernel: algorithmic FLOPs (or bytes) per
+              launch / its mean duration from HIP events on the launch stream;
+              traffic = HBM bytes per launch from FETCH_SIZE / WRITE_SIZE counters
+              (profiles/traffic_*.txt), null when the kernel sources changed since
+  cpu_baseline the fp64 CPU oracle timed on a bounded sample of rows of the same
+              workload, scaled to the same unit
+  check       GPU vs oracle on those sampled rows
+
+Algorithmic work: 4*D FLOPs per visible (query row, key, head) triple (2*D for
+QK^T, 2*Dv for PV); masked, padded and skipped pairs count nothing. Decode
+bytes: every valid K and V element once, plus q, O and LSE.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, REPO)
+
+METRIC = "attn fwd TFLOP/s & % MI355X bf16 MFMA peak; decode GB/s & % HBM peak"
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+DECODE = ("c5b",)
+
+DESCRIPTION = {
+    "c1": "non-causal MHA [1,257,8,128]",
+    "c2": "non-causal MHA [1,20480,56,128] (video joint attention)",
+    "c3": "varlen causal GQA 32/8 D128 + rel_bias E256, 8 seqs len U[512,8192]",
+    "c4a": "self-attention [256,10000,6,64]",
+    "c4b": "feature attention [100,100000,4,16]",
+    "c4c": "cross attention q[1,1000,6,64] k/v[1,1e6,6,64], split-KV heuristic",
+    "c5a": "8:1 pack-GQA D256 q[4,1024,8,256] k/v[4,2048,1,256] seqused_k U[600,2048]",
+    "c5b": "D256 decode q[32,1,8,256] k/v[32,131072,1,256] causal, split-KV + combine",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def lengths(spec, x):
+    if spec.varlen:
+        ql = np.diff(x["cu_seqlens_q"].astype(np.int64))
+        kl = np.diff(x["cu_seqlens_k"].astype(np.int64))
+    else:
+        ql = np.full(spec.B, spec.Sq, dtype=np.int64)
+        kl = np.full(spec.B, spec.Sk, dtype=np.int64)
+    if "seqused_k" in x:
+        kl = x["seqused_k"].astype(np.int64)
+    return ql, kl
+
+
+def visible_keys(causal, ql, kl):
+    """Visible keys of each query row of one sequence (bottom-right causal alignment)."""
+    if not causal:
+        return np.full(ql, kl, dtype=np.int64)
+    return np.clip(np.arange(ql, dtype=np.int64) + (kl - ql) + 1, 0, kl)
+
+
+def algorithmic_flops(spec, x):
+    ql, kl = lengths(spec, x)
+    pairs = sum(int(visible_keys(spec.causal, int(a), int(b)).sum()) for a, b in zip(ql, kl))
+    return pairs * spec.Hq * (2 * spec.D + 2 * spec.Dv)
+
+
+def algorithmic_bytes(spec, x):
+    ql, kl = lengths(spec, x)
+    kv = int(kl.sum()) * spec.Hkv * (spec.D + spec.Dv) * 2
+    rows = int(ql.sum()) * spec.Hq
+    return kv + rows * (spec.D * 2 + spec.Dv * 2 + 4)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(REPO, "exact_attention_forward_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, dtype):
+    """HBM bytes per launch from committed counter data, if taken on the current kernel sources."""
+    path = os.path.join(REPO, "profiles", f"traffic_{workload}_{dtype}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                a, b = line.split("=", 1)
+                kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def sample_rows(spec, x, n, seed=12345):
+    """Deterministic sample of (b, h, i) rows spread over batches, heads and positions."""
+    from workloads import gen
+    ql, _ = lengths(spec, x)
+    rng = gen.make_rng(seed)
+    bs = np.nonzero(ql > 0)[0]
+    b = rng.choice(bs, size=n)
+    h = rng.integers(0, spec.Hq, size=n)
+    i = (rng.random(n) * ql[b]).astype(np.int64)
+    return np.stack([b, h, i], axis=1).astype(np.int32)
+
+
+def cpu_baseline(spec, x, out, lse, target_s, threads):
+    """Time the oracle on a bounded row sample; also compare those rows with the GPU result."""
+    from oracle import oracle as oracle_mod
+    from workloads import gen
+    ql, kl = lengths(spec, x)
+    kw = dict(dtype=spec.dtype, B=spec.B, Sq=spec.Sq, Sk=spec.Sk, Hq=spec.Hq, Hkv=spec.Hkv,
+              D=spec.D, Dv=spec.Dv, scale=spec.scale, causal=spec.causal,
+              cu_seqlens_q=x.get("cu_seqlens_q"), cu_seqlens_k=x.get("cu_seqlens_k"),
+              seqused_k=x.get("seqused_k"), rel_bias=x.get("rel_bias"), threads=threads)
+    cu = x.get("cu_seqlens_q")
+
+    def row_flops(rows):
+        tot = 0
+        for b, _, i in rows:
+            vk = visible_keys(spec.causal, int(ql[b]), int(kl[b]))
+            tot += int(vk[i])
+        return tot * (2 * spec.D + 2 * spec.Dv)
+
+    n = max(threads, 8)
+    rows = sample_rows(spec, x, n)
+    t0 = time.perf_counter()
+    oracle_mod.attn_rows(x["q"], x["k"], x["v"], rows=rows, **kw)
+    dt = time.perf_counter() - t0
+    n = int(min(200000, max(n, n * target_s / max(dt, 1e-3))))
+    rows = sample_rows(spec, x, n, seed=777)
+    t0 = time.perf_counter()
+    o_ref, l_ref = oracle_mod.attn_rows(x["q"], x["k"], x["v"], rows=rows, **kw)
+    dt = time.perf_counter() - t0
+    flops = row_flops(rows)
+    # compare the sampled rows with the GPU output
+    b, h, i = (rows[:, c].astype(np.int64) for c in range(3))
+    import torch
+    if cu is not None:
+        t = cu.astype(np.int64)[b] + i
+        og = out.view(torch.int16)[torch.from_numpy(t).cuda(), torch.from_numpy(h).cuda()]
+        lg = lse.cpu().numpy()[h, t]
+    else:
+        og = out.view(torch.int16)[torch.from_numpy(b).cuda(), torch.from_numpy(i).cuda(),
+                                   torch.from_numpy(h).cuda()]
+        lg = lse.cpu().numpy()[b, h, i]
+    og = gen.bits_to_f32(og.cpu().numpy().view(np.uint16), spec.dtype).astype(np.float64)
+    fin = np.isfinite(l_ref)
+    check = {"rows": int(n),
+             "o_max_abs_err": float(np.abs(og - o_ref).max()) if n else 0.0,
+             "lse_max_abs_err": float(np.abs(lg[fin] - l_ref[fin]).max()) if fin.any() else 0.0}
+    sample = (f"{n} (batch, head, query) rows drawn uniformly from the workload, each over all "
+              f"of its visible keys ({flops / n:.3g} FLOP per row on average)")
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3), "sample_flop": flops}, check
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", choices=sorted(DESCRIPTION))
+    ap.add_argument("--dtype", default=None, choices=["bf16", "fp16"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB elementwise copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the path would "
+              "shard over (batch, KV head) with no exchange, or over the key range with one "
+              "LSE combine step", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_forward_amd as fa
+    from workloads import configs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    fa.load()
+    spec = configs.workload(args.workload, args.dtype)
+    log(f"generating {args.workload} ({DESCRIPTION[args.workload]}) {spec.dtype}")
+    x = configs.make_inputs(spec)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[spec.dtype]
+
+    def dev16(a):
+        return torch.from_numpy(a.view(np.int16)).cuda().view(tdt)
+
+    q, k, v = dev16(x["q"]), dev16(x["k"]), dev16(x["v"])
+    kw = dict(causal=spec.causal, scale=spec.scale, num_splits=spec.num_splits,
+              pack_gqa=spec.pack_gqa)
+    varlen = spec.varlen
+    if varlen:
+        kw.update(cu_seqlens_q=torch.from_numpy(x["cu_seqlens_q"]).cuda(),
+                  cu_seqlens_k=torch.from_numpy(x["cu_seqlens_k"]).cuda(),
+                  max_seqlen_q=x["max_seqlen_q"], max_seqlen_k=x["max_seqlen_k"])
+    if "seqused_k" in x:
+        kw["seqused_k"] = torch.from_numpy(x["seqused_k"]).cuda()
+    if "rel_bias" in x:
+        kw["rel_bias"] = dev16(x["rel_bias"])
+    # preallocate everything: the timed calls allocate nothing
+    out, lse = fa.attn_fwd(q, k, v, **kw)
+    ns = fa.num_splits(spec.B, spec.Sq, spec.Sk, spec.Hq, spec.Hkv, spec.D, spec.Dv,
+                       is_varlen=varlen, max_seqlen_q=x.get("max_seqlen_q", 0),
+                       max_seqlen_k=x.get("max_seqlen_k", 0), pack_gqa=spec.pack_gqa,
+                       requested=spec.num_splits)
+    ws = None
+    if ns > 1:
+        ws = torch.empty(fa.workspace_size(spec.B, spec.Sq, spec.Hq, spec.Dv, is_varlen=varlen,
+                                           splits=ns), dtype=torch.uint8, device="cuda")
+    kw.update(out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.float16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x elementwise copy of 1 GiB")
+
+    for _ in range(args.warmup):
+        fa.attn_fwd(q, k, v, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        fa.attn_fwd(q, k, v, **kw)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms_step = wall * 1e3 / args.steps
+    mean_call_ms = float(np.mean(per_call_ms))
+
+    flops = algorithmic_flops(spec, x)
+    decode = args.workload in DECODE
+    if decode:
+        nbytes = algorithmic_bytes(spec, x)
+        value = nbytes / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = nbytes / (mean_call_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        value = flops / (ms_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = flops / (mean_call_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_MFMA_TFLOPS}
+    roof["traffic"] = read_traffic(args.workload, spec.dtype)
+    roof["kernel_ms"] = mean_call_ms
+    roof["kernels_per_launch"] = 2 if ns > 1 else 1
+    log(f"{args.workload}: {ms_step:.4f} ms/step wall, {mean_call_ms:.4f} ms/call events, "
+        f"{flops:.4g} FLOP, splits={ns}")
+
+    result = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {DESCRIPTION[args.workload]}", "B": spec.B,
+                   "Sq": spec.Sq, "Sk": spec.Sk, "Hq": spec.Hq, "Hkv": spec.Hkv, "D": spec.D,
+                   "causal": spec.causal, "varlen": varlen, "rel_extent": spec.rel_extent,
+                   "num_splits": ns, "algorithmic_flop": flops, "seed": spec.seed,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        threads = min(16, os.cpu_count() or 1)
+        cb, check = cpu_baseline(spec, x, out, lse, args.cpu_seconds, threads)
+        if decode:
+            # the sample's share of the algorithmic bytes, by its share of the visible pairs
+            cb["value"] = nbytes * (cb["sample_flop"] / flops) / cb["seconds"] / 1e9
+            cb["unit"] = "GB/s"
+        result["cpu_baseline"] = cb
+        result["check"] = check
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
