@@ -96,6 +96,8 @@ attn_status_t validate(const void* q, const void* k, const void* v, void* out, f
     if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Dv <= 0) return ATTN_ERR_BAD_SHAPE;
     if (D != Dv || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
     if (Hq % Hkv) return ATTN_ERR_BAD_GQA;
+    // a K/V tile (64 keys) must span fewer than 2^31 bytes: buffer offsets are 32-bit
+    if ((long long)Hkv * D > (1LL << 23)) return ATTN_ERR_BAD_SHAPE;
     if (!isfinite(scale)) return ATTN_ERR_BAD_SCALE;
     if (pack_gqa < -1 || pack_gqa > 1) return ATTN_ERR_BAD_ARG;
     if ((cu_q == nullptr) != (cu_k == nullptr)) return ATTN_ERR_BAD_VARLEN;

@@ -46,6 +46,7 @@ typedef __attribute__((address_space(3))) s16x4v lds_s16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLoThresh = 32.f;  // rows with a smaller softmax normaliser get the P remainder MFMA
+constexpr float kTau = 8.f;        // O / l are rescaled only when the row max grows by more than 2^kTau
 
 template <bool BF>
 struct Elem;
@@ -90,26 +91,52 @@ struct Tile {
     static constexpr int NC = D / 16;             // 16-wide steps of the QK contraction
     static constexpr int NDT = (D + 31) / 32;     // 32-wide dv blocks of O^T
     static constexpr int NKB = BN / 32;           // 32-key blocks of S^T
-    static constexpr int KSTRIDE = D * 2 + 16;    // bytes per K row in LDS (padded)
-    static constexpr int K_BYTES = BN * KSTRIDE;
-    static constexpr int V_BYTES = BN * D * 2;    // 4x4-blocked, unpadded
-    static constexpr int STAGE = K_BYTES + V_BYTES;
-    static constexpr int LDS = 2 * STAGE;
-    static constexpr int CHUNKS = BN * D / 8;     // 16-byte chunks per K (or V) tile
-    static constexpr int NCH = (CHUNKS + NT - 1) / NT;
+    static constexpr int NG = D / 8;              // 16-byte granules per K / V row
+    static constexpr int SWZ_DIV = NG >= 16 ? 1 : 16 / NG;
+    static constexpr int TILE_BYTES = BN * D * 2; // one K or V tile in LDS
+    static constexpr int PREFETCH = 3;            // tiles loaded ahead of the one being consumed
+    static constexpr int NB = PREFETCH + 1;       // LDS ring stages, each a K tile and a V tile
+    // Two independent work-groups per CU for D <= 128 (each wave then fits in 256
+    // registers and the SIMD interleaves one group's MFMAs with the other's softmax);
+    // at D = 256 a wave needs more than 256 registers, so one group per CU.
+    static constexpr int WG_PER_CU = D <= 128 ? 2 : 1;
+    static constexpr int LDS = NB * 2 * TILE_BYTES;
+    static constexpr int GRANULES = BN * NG;      // 16-byte granules per tile
+    static constexpr int LOADS = (GRANULES + NT - 1) / NT;  // per thread, per K (or V) tile
+    static constexpr int VM_PER_TILE = 2 * LOADS;           // buffer loads a wave issues per tile
     static_assert(D == 16 || D == 64 || D == 128 || D == 256, "head dim");
-    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(LDS * WG_PER_CU <= 160 * 1024, "LDS budget");
+    static_assert(GRANULES % 64 == 0, "whole waves per load instruction");
 };
 
 // Position of element r (0..15) of a 32x32 MFMA accumulator in lane half hf:
 // row offset within the 32-row block (the "M" index).
 __device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
+// K tile in LDS: granule (key, c) of 8 elements sits at key * NG + (c ^ swizzle(key)),
+// so the 16 rows read by one ds_read_b128 pass fall in 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k_granule(int key, int c) {
+    using T = Tile<D>;
+    return key * T::NG + (c ^ ((key / T::SWZ_DIV) % T::NG));
+}
+
+// V tile in LDS, 4-key blocks: granule (key, 8-wide dv chunk q8) sits at
+// ((key / 4) * NG + q8) * 4 + key % 4. A ds_read_b64_tr_b16 group then reads
+// 4 keys x 16 dv = 128 contiguous bytes.
+template <int D>
+__device__ __forceinline__ int v_granule(int key, int q8) {
+    return ((key >> 2) * Tile<D>::NG + q8) * 4 + (key & 3);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT>
-__global__ void __launch_bounds__(256, 1) attn_fwd_kernel(const FwdParams p) {
+__global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const FwdParams p) {
     using T = Tile<D>;
     using E = Elem<BF>;
     typedef typename E::v8 v8;
+    typedef f32x16 STile[T::NQB][T::NKB];
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x;
@@ -205,11 +232,16 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_kernel(const FwdParams p) {
         }
     }
 
+    // Online-softmax state per row, log2 domain. m_run is the running row max;
+    // m_used is the max the exponentials and O are currently referred to. O and
+    // l are only rescaled when m_run exceeds m_used by more than kTau, so
+    // p = 2^(t - m_used) <= 2^kTau and the rescale is rare after the first tiles.
     f32x16 o[T::NQB][T::NDT];
-    float m_run[T::NQB], l_run[T::NQB];
+    float m_run[T::NQB], m_used[T::NQB], l_run[T::NQB];
 #pragma unroll
     for (int qb = 0; qb < T::NQB; qb++) {
         m_run[qb] = -INFINITY;
+        m_used[qb] = -INFINITY;
         l_run[qb] = 0.f;
 #pragma unroll
         for (int dt = 0; dt < T::NDT; dt++)
@@ -217,58 +249,41 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_kernel(const FwdParams p) {
             for (int r = 0; r < 16; r++) o[qb][dt][r] = 0.f;
     }
 
+    // ---- K/V tiles: buffer loads straight into LDS (no register staging) ----
+    // Rows past k_len lie outside the buffer range, so the hardware writes zeros
+    // for them: padding (even NaN) never reaches the MFMAs.
     const uint16_t* kbase = p.k + (k_off * p.Hkv + hk) * (long long)D;
     const uint16_t* vbase = p.v + (k_off * p.Hkv + hk) * (long long)D;
-    const long long kv_row_stride = (long long)p.Hkv * D;  // elements between consecutive keys
+    const int row_bytes = p.Hkv * D * 2;  // bytes between consecutive keys
+    auto kstage = [&](int st) __attribute__((always_inline)) { return smem + st * 2 * T::TILE_BYTES; };
+    auto vstage = [&](int st) __attribute__((always_inline)) { return smem + st * 2 * T::TILE_BYTES + T::TILE_BYTES; };
 
-    // ---- global -> register staging of one K/V tile ----
-    u32x4 kst[T::NCH], vst[T::NCH];
-    auto load_tile = [&](int kb) {
+    auto issue_tile = [&](const uint16_t* base, int kb, char* dst, bool is_v) __attribute__((always_inline)) {
         const int j0 = kb * T::BN;
+        const int rows = max(0, min(T::BN, k_len - j0));
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(base + (long long)j0 * p.Hkv * D), (short)0, rows * row_bytes, 0x00020000);
 #pragma unroll
-        for (int u = 0; u < T::NCH; u++) {
-            const int c = tid + u * T::NT;
-            kst[u] = u32x4{0u, 0u, 0u, 0u};
-            vst[u] = u32x4{0u, 0u, 0u, 0u};
-            if (c < T::CHUNKS) {
-                // K: row-major chunks (8 consecutive elements of one key)
-                const int kkey = c / (D / 8), kcol = c % (D / 8);
-                if (j0 + kkey < k_len)
-                    kst[u] = *(const u32x4*)(kbase + (long long)(j0 + kkey) * kv_row_stride + kcol * 8);
-                // V: four consecutive keys per lane quad, for the blocked LDS layout
-                const int vkr = c & 3, vcol = (c >> 2) % (D / 8), vkq = c / (4 * (D / 8));
-                const int vkey = vkq * 4 + vkr;
-                if (j0 + vkey < k_len)
-                    vst[u] = *(const u32x4*)(vbase + (long long)(j0 + vkey) * kv_row_stride + vcol * 8);
-            }
-        }
-    };
-    auto store_tile = [&](int stage) {
-        char* kl = smem + stage * T::STAGE;
-        char* vl = kl + T::K_BYTES;
-#pragma unroll
-        for (int u = 0; u < T::NCH; u++) {
-            const int c = tid + u * T::NT;
-            if (c < T::CHUNKS) {
-                const int kkey = c / (D / 8), kcol = c % (D / 8);
-                *(u32x4*)(kl + kkey * T::KSTRIDE + kcol * 16) = kst[u];
-                const int vkr = c & 3, vcol = (c >> 2) % (D / 8), vkq = c / (4 * (D / 8));
-                // V[key][4*dq .. 4*dq+3] lives in block (key/4, dq) at row key%4
-                char* vb = vl + (vkq * (D / 4) + 2 * vcol) * 32 + vkr * 8;
-                *(u32x2*)(vb) = u32x2{vst[u][0], vst[u][1]};
-                *(u32x2*)(vb + 32) = u32x2{vst[u][2], vst[u][3]};
+        for (int u = 0; u < T::LOADS; u++) {
+            const int g0 = T::NT * u + 64 * wave;  // first granule of this wave's instruction
+            if (T::GRANULES % T::NT == 0 || g0 < T::GRANULES) {
+                const int g = g0 + lane;
+                int key, c;
+                if (!is_v) {
+                    key = g / T::NG;
+                    c = (g % T::NG) ^ ((key / T::SWZ_DIV) % T::NG);
+                } else {
+                    key = (g / (4 * T::NG)) * 4 + (g & 3);
+                    c = (g >> 2) % T::NG;
+                }
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + g0 * 16), 16,
+                                                         key * row_bytes + c * 16, 0, 0, 0);
             }
         }
     };
 
-    // ---- per-tile compute ----
-    auto compute_tile = [&](int kb, int stage) {
-        const int j0 = kb * T::BN;
-        const char* kl = smem + stage * T::STAGE;
-        const char* vl = kl + T::K_BYTES;
-
-        // S^T = K Q^T
-        f32x16 s[T::NQB][T::NKB];
+    // S^T = K Q^T for one key tile
+    auto qk = [&](const char* kl, STile& s) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++)
 #pragma unroll
@@ -277,164 +292,282 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_kernel(const FwdParams p) {
                 for (int r = 0; r < 16; r++) s[qb][kb2][r] = 0.f;
 #pragma unroll
         for (int kb2 = 0; kb2 < T::NKB; kb2++) {
-            const char* krow = kl + (kb2 * 32 + l32) * T::KSTRIDE + 16 * hf;
+            const int key = kb2 * 32 + l32;
 #pragma unroll
             for (int c = 0; c < T::NC; c++) {
-                const v8 a = *(const v8*)(krow + 32 * c);
+                const v8 a = *(const v8*)(kl + k_granule<D>(key, 2 * c + hf) * 16);
 #pragma unroll
                 for (int qb = 0; qb < T::NQB; qb++) s[qb][kb2] = E::mma(a, qf[qb][c], s[qb][kb2]);
             }
         }
+    };
 
-        // which per-element work this tile needs (uniform across the work-group)
-        const bool need_kmask = (j0 + T::BN > k_len);
-        const bool need_causal = CAUSAL && (j0 + T::BN - 1 > i_lo + delta);
-        const bool need_mask = need_kmask || need_causal;
-        const bool band = BIAS && (i_hi + delta - j0 >= 0) && (i_lo + delta - (j0 + T::BN - 1) < p.E);
+    auto partner_max = [](float x) __attribute__((always_inline)) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    };
+    auto partner_sum = [](float x) __attribute__((always_inline)) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    };
 
-        // online softmax, log2 domain: t = s * scale * log2(e) (+ bias * log2(e))
+    // Raise m_used to m_run in the rows where it fell more than kTau behind; l is
+    // rescaled here, O later (once, just before PV) by alpha. The decision is per
+    // row, so a row's arithmetic never depends on the other rows of its wave; the
+    // O multiply runs when any row of the wave needs it (alpha = 1 elsewhere).
+    float alpha[T::NQB];
+    bool rescale_o = false;
+    auto update_used_max = [&]() __attribute__((always_inline)) {
+        bool need = false;
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
-            float mt = -INFINITY;
-            const int i = qi[qb];
-            if (need_mask || band) {
-                const uint16_t* brow = nullptr;
-                if (BIAS) brow = p.bias + ((q_off + i) * p.Hq + qh[qb]) * (long long)p.E;
-#pragma unroll
-                for (int kb2 = 0; kb2 < T::NKB; kb2++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int j = j0 + kb2 * 32 + acc_row(r, hf);
-                        float t = s[qb][kb2][r] * p.c2;
-                        const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
-                        if (BIAS && band) {
-                            const int d = i + delta - j;
-                            if (vis && qvalid[qb] && d >= 0 && d < p.E) t += E::widen(brow[d]) * kLog2e;
-                        }
-                        t = vis ? t : -INFINITY;
-                        s[qb][kb2][r] = t;
-                        mt = fmaxf(mt, t);
-                    }
-            } else {
-#pragma unroll
-                for (int kb2 = 0; kb2 < T::NKB; kb2++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const float t = s[qb][kb2][r] * p.c2;
-                        s[qb][kb2][r] = t;
-                        mt = fmaxf(mt, t);
-                    }
+            alpha[qb] = 1.f;
+            if (m_run[qb] > m_used[qb] + kTau) {  // false while nothing is visible (m_run = -inf)
+                alpha[qb] = __builtin_amdgcn_exp2f(m_used[qb] - m_run[qb]);
+                m_used[qb] = m_run[qb];
+                l_run[qb] *= alpha[qb];
+                need = true;
             }
-            {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-                mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            }
-            const float m_new = fmaxf(m_run[qb], mt);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
-            m_run[qb] = m_new;
+        }
+        rescale_o = __any(need);
+    };
+    auto rescale_acc = [&]() __attribute__((always_inline)) {
+        if (rescale_o) {
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++)
+#pragma unroll
+                for (int dt = 0; dt < T::NDT; dt++) {
+                    f32x16 x = o[qb][dt];
+                    x *= alpha[qb];
+                    if (T::WG_PER_CU == 1) asm volatile("" : "+a"(x));  // one block at a time
+                    o[qb][dt] = x;
+                }
+        }
+    };
+
+    // Each tile's softmax runs in two phases around the (rare) O rescale:
+    // phase 1 updates the row maxima and decides the rescale, phase 2 turns the
+    // scores into p = 2^(s * c2 + b - m_used) and adds them to l.
+    //
+    // Unmasked tile, positive scale: the max of s * c2 is max(s) * c2 exactly
+    // (rounding is monotonic), and p is one FMA + exp2.
+    auto max_fast = [&](STile& s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[qb][kb2][r]);
+            m_run[qb] = fmaxf(m_run[qb], partner_max(mx) * p.c2);
+        }
+        update_used_max();
+    };
+    auto exp_fast = [&](STile& s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) {
+            const float mu = m_used[qb];
             float rs = 0.f;
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const float pv = __builtin_amdgcn_exp2f(s[qb][kb2][r] - m_use);
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, -mu));
                     s[qb][kb2][r] = pv;
                     rs += pv;
                 }
-            l_run[qb] = l_run[qb] * alpha + rs;
-#pragma unroll
-            for (int dt = 0; dt < T::NDT; dt++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) o[qb][dt][r] *= alpha;
+            l_run[qb] += rs;
         }
+    };
 
-        // bf16 P carries a 2^-9 relative rounding error; for a row whose normaliser
-        // is still small (few keys hold its weight) that error can reach the output
-        // tolerance, so such rows also feed the remainder P - bf16(P) through a
-        // second MFMA. A row with normaliser l has at least l effective keys, and
-        // the error shrinks like 2^-9 / sqrt(3 l); rows at or above kLoThresh skip it.
+    // Tiles that cross the key bound, the causal diagonal or the bias band (or scale <= 0).
+    // Per element the arithmetic is the fast path's (one FMA into exp2, with the
+    // bias term folded into the addend), so the result of a row does not depend on
+    // which path a tile takes; masked keys get p = 0. Phase 1 leaves the bias term
+    // (times log2 e) in s for visible keys and -inf for masked ones; phase 2
+    // recomputes s * c2 from the MFMA result kept in sraw.
+    float bt[T::NQB][T::NKB][16];
+    auto max_slow = [&](STile& s, int j0, bool band) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) {
+            float mx = -INFINITY;
+            const int i = qi[qb];
+            const uint16_t* brow = nullptr;
+            if (BIAS) brow = p.bias + ((q_off + i) * p.Hq + qh[qb]) * (long long)p.E;
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int j = j0 + kb2 * 32 + acc_row(r, hf);
+                    const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
+                    float b2 = 0.f;
+                    if (BIAS && band) {
+                        const int d = i + delta - j;
+                        if (vis && qvalid[qb] && d >= 0 && d < p.E) b2 = E::widen(brow[d]) * kLog2e;
+                    }
+                    bt[qb][kb2][r] = vis ? b2 : -INFINITY;
+                    mx = fmaxf(mx, vis ? __builtin_fmaf(s[qb][kb2][r], p.c2, b2) : -INFINITY);
+                }
+            m_run[qb] = fmaxf(m_run[qb], partner_max(mx));
+        }
+        update_used_max();
+    };
+    auto exp_slow = [&](STile& s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) {
+            const float mu = m_used[qb] == -INFINITY ? 0.f : m_used[qb];
+            float rs = 0.f;
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const float b2 = bt[qb][kb2][r];
+                    const float pv = b2 == -INFINITY ? 0.f
+                                                     : __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, b2 - mu));
+                    s[qb][kb2][r] = pv;
+                    rs += pv;
+                }
+            l_run[qb] += rs;
+        }
+    };
+
+    // O^T += V^T P^T, 16 keys per MFMA step. bf16 P carries a 2^-9 relative
+    // rounding error; for a row whose normaliser is still small (few keys hold
+    // its weight) that error can reach the output tolerance, so such rows also
+    // feed the remainder P - bf16(P) through a second MFMA. A row with
+    // normaliser l (max weight 1) has at least l effective keys, and the error
+    // shrinks like 2^-9 / sqrt(3 l); rows at or above kLoThresh skip it.
+    auto pv = [&](const char* vl, STile& s) __attribute__((always_inline)) {
         bool need_lo[T::NQB];
         bool any_lo = false;
         if (BF) {
 #pragma unroll
             for (int qb = 0; qb < T::NQB; qb++) {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[qb]),
-                                                                 __float_as_uint(l_run[qb]), false, false);
-                need_lo[qb] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]) < kLoThresh;
+                const float lt = partner_sum(l_run[qb]) * __builtin_amdgcn_exp2f(m_used[qb] - m_run[qb]);
+                need_lo[qb] = lt < kLoThresh;
                 any_lo = any_lo || need_lo[qb];
             }
             any_lo = __any(any_lo);
         }
-
-        // O^T += V^T P^T, 16 keys per MFMA step
+        const int g = lane >> 4, jj = lane & 15;
+        auto vfrag = [&](int t, int dt) __attribute__((always_inline)) {
+            // lanes of group g receive dv = 32dt + 16(g&1) + jj; keys 16t + 4hf (+8)
+            int dv0 = 32 * dt + 16 * (g & 1);
+            const bool dv_ok = dv0 < D;
+            if (!dv_ok) dv0 = 0;  // D = 16: the upper half of the dv block is padding
+            const int kq = 4 * t + hf;  // (16t + 4hf) / 4
+            const char* pa = vl + v_granule<D>(4 * kq + (jj >> 2), (dv0 >> 3) + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
+            const char* pb = pa + 2 * T::NG * 4 * 16;  // keys + 8 = two 4-key blocks later
+            const s16x4v ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
+            const s16x4v rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pb);
+            u32x4 w;
+            w[0] = __builtin_bit_cast(u32x2, ra)[0];
+            w[1] = __builtin_bit_cast(u32x2, ra)[1];
+            w[2] = __builtin_bit_cast(u32x2, rb)[0];
+            w[3] = __builtin_bit_cast(u32x2, rb)[1];
+            if (!dv_ok) w = u32x4{0u, 0u, 0u, 0u};
+            return __builtin_bit_cast(v8, w);
+        };
+        if (BF && any_lo) {
 #pragma unroll
-        for (int t = 0; t < T::BN / 16; t++) {
-            v8 pt[T::NQB], ptl[T::NQB];
+            for (int t = 0; t < T::BN / 16; t++) {
+                v8 pt[T::NQB], ptl[T::NQB];
 #pragma unroll
-            for (int qb = 0; qb < T::NQB; qb++)
+                for (int qb = 0; qb < T::NQB; qb++)
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const float pv = s[qb][t >> 1][8 * (t & 1) + e];
-                    pt[qb][e] = E::to_elem(pv);
-                    if (BF && any_lo) ptl[qb][e] = E::to_elem(need_lo[qb] ? pv - (float)pt[qb][e] : 0.f);
+                    for (int e = 0; e < 8; e++) {
+                        const float pvv = s[qb][t >> 1][8 * (t & 1) + e];
+                        pt[qb][e] = E::to_elem(pvv);
+                        ptl[qb][e] = E::to_elem(need_lo[qb] ? pvv - (float)pt[qb][e] : 0.f);
+                    }
+#pragma unroll
+                for (int dt = 0; dt < T::NDT; dt++) {
+                    const v8 a = vfrag(t, dt);
+#pragma unroll
+                    for (int qb = 0; qb < T::NQB; qb++) {
+                        o[qb][dt] = E::mma(a, pt[qb], o[qb][dt]);
+                        o[qb][dt] = E::mma(a, ptl[qb], o[qb][dt]);
+                    }
                 }
-            const int g = lane >> 4, jj = lane & 15;
+            }
+        } else {
 #pragma unroll
-            for (int dt = 0; dt < T::NDT; dt++) {
-                // lanes of group g receive dv = 32dt + 16(g&1) + (lane&15); keys 16t + 4hf (+8)
-                int dv0 = 32 * dt + 16 * (g & 1);
-                const bool dv_ok = dv0 < D;
-                if (!dv_ok) dv0 = 0;  // D = 16: the upper half of the dv block is padding
-                const int key_a = 16 * t + 4 * hf;
-                const char* pa = vl + ((key_a >> 2) * (D / 4) + (dv0 >> 2) + (jj & 3)) * 32 + (jj >> 2) * 8;
-                const char* pb = pa + 2 * (D / 4) * 32;  // keys + 8 = two key-quads later
-                const s16x4v ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
-                const s16x4v rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pb);
-                u32x4 w;
-                w[0] = __builtin_bit_cast(u32x2, ra)[0];
-                w[1] = __builtin_bit_cast(u32x2, ra)[1];
-                w[2] = __builtin_bit_cast(u32x2, rb)[0];
-                w[3] = __builtin_bit_cast(u32x2, rb)[1];
-                if (!dv_ok) w = u32x4{0u, 0u, 0u, 0u};
-                const v8 a = __builtin_bit_cast(v8, w);
+            for (int t = 0; t < T::BN / 16; t++) {
+                v8 pt[T::NQB];
 #pragma unroll
-                for (int qb = 0; qb < T::NQB; qb++) {
-                    o[qb][dt] = E::mma(a, pt[qb], o[qb][dt]);
-                    if (BF && any_lo) o[qb][dt] = E::mma(a, ptl[qb], o[qb][dt]);
+                for (int qb = 0; qb < T::NQB; qb++)
+#pragma unroll
+                    for (int e = 0; e < 8; e++) pt[qb][e] = E::to_elem(s[qb][t >> 1][8 * (t & 1) + e]);
+#pragma unroll
+                for (int dt = 0; dt < T::NDT; dt++) {
+                    const v8 a = vfrag(t, dt);
+#pragma unroll
+                    for (int qb = 0; qb < T::NQB; qb++) o[qb][dt] = E::mma(a, pt[qb], o[qb][dt]);
                 }
             }
         }
     };
 
-    // ---- main loop: double-buffered K/V tiles ----
+    // ---- main loop over key tiles ----
+    // Tile j (its K and V) lives in ring stage (j - kb_begin) % NB and is loaded
+    // PREFETCH iterations before it is used. Iteration j: loads of tile
+    // j + PREFETCH go out; S^T = K Q^T; softmax; O^T += V^T P^T; then each wave
+    // waits until tile j+1 has landed (vmcnt counts this wave's buffer loads,
+    // which complete in order) and the work-group meets at one barrier.
+    auto wait_tiles_after_next = [&](int n_after) __attribute__((always_inline)) {
+        // s_waitcnt vmcnt(n_after * VM_PER_TILE); expcnt / lgkmcnt unconstrained
+        constexpr int L = T::VM_PER_TILE;
+        static_assert((T::PREFETCH - 1) * L < 64, "vmcnt field");
+#define MI355_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
+        if (n_after <= 0) MI355_WAIT_VM(0);
+        else if (n_after == 1) MI355_WAIT_VM(L);
+        else MI355_WAIT_VM(2 * L);
+#undef MI355_WAIT_VM
+    };
+    static_assert(T::PREFETCH == 3, "wait_tiles_after_next covers up to two later tiles");
+    auto issue = [&](int j) __attribute__((always_inline)) {
+        const int st = (j - kb_begin) % T::NB;
+        issue_tile(kbase, j, kstage(st), false);
+        issue_tile(vbase, j, vstage(st), true);
+    };
     if (kb_begin < kb_end) {
-        load_tile(kb_begin);
-        store_tile(0);
+        const int first_end = min(kb_begin + T::PREFETCH, kb_end);
+        for (int j = kb_begin; j < first_end; j++) issue(j);
+        wait_tiles_after_next(first_end - 1 - kb_begin);  // tile kb_begin has landed
         __syncthreads();
         for (int kb = kb_begin; kb < kb_end; kb++) {
-            const int stage = (kb - kb_begin) & 1;
-            const bool more = kb + 1 < kb_end;
-            if (more) load_tile(kb + 1);
-            compute_tile(kb, stage);
-            if (more) store_tile(stage ^ 1);
+            const int r = kb - kb_begin;
+            if (kb + T::PREFETCH < kb_end) issue(kb + T::PREFETCH);
+            const int j0 = kb * T::BN;
+            const bool need_mask = (j0 + T::BN > k_len) || (CAUSAL && (j0 + T::BN - 1 > i_lo + delta));
+            const bool band = BIAS && (i_hi + delta - j0 >= 0) && (i_lo + delta - (j0 + T::BN - 1) < p.E);
+            STile s;
+            qk(kstage(r % T::NB), s);
+            if (!need_mask && !band && p.c2 > 0.f) {
+                max_fast(s);
+                rescale_acc();
+                exp_fast(s);
+            } else {
+                max_slow(s, j0, band);
+                rescale_acc();
+                exp_slow(s);
+            }
+            pv(vstage(r % T::NB), s);
+            // tiles issued after kb+1: kb+2 .. min(kb+PREFETCH, kb_end-1)
+            wait_tiles_after_next(min(kb + T::PREFETCH, kb_end - 1) - (kb + 1));
             __syncthreads();
         }
     }
 
-    // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2 ----
+    // ---- epilogue: O = O_acc / l, LSE = (m_used + log2 l) ln 2 ----
 #pragma unroll
     for (int qb = 0; qb < T::NQB; qb++) {
-        float lt = l_run[qb];
-        {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt), false, false);
-            lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        }
+        const float lt = partner_sum(l_run[qb]);
         if (!qvalid[qb]) continue;
         const int i = qi[qb], h = qh[qb];
         const bool nonempty = lt > 0.f;
         const float inv = nonempty ? 1.0f / lt : 0.f;
-        const float lse_v = nonempty ? (m_run[qb] + log2f(lt)) * kLn2 : -INFINITY;
+        const float lse_v = nonempty ? (m_used[qb] + log2f(lt)) * kLn2 : -INFINITY;
         const long long orow = (q_off + i) * p.Hq + h;  // row of the [rows_q, Hq, Dv] output
         const long long lidx = VARLEN ? (long long)h * p.rows_q + q_off + i
                                       : ((long long)b * p.Hq + h) * p.Sq + i;

@@ -14,9 +14,9 @@ struct TileGeom {
     int bn;    // keys per K/V tile
 };
 
-__host__ __device__ constexpr int tile_nqb(int D) { return D <= 128 ? 2 : 1; }
+__host__ __device__ constexpr int tile_nqb(int /*D*/) { return 1; }
 __host__ __device__ constexpr int tile_bm(int D) { return 4 * 32 * tile_nqb(D); }
-__host__ __device__ constexpr int tile_bn(int /*D*/) { return 64; }
+__host__ __device__ constexpr int tile_bn(int /*D*/) { return 32; }
 
 struct FwdParams {
     const uint16_t* q;

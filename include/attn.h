@@ -104,7 +104,8 @@ typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1 } attn_dtype_t;
  *   the combine kernel runs on the same stream before the call returns.
  *   workspace may be NULL when no split is used.
  * Alignment: q, k, v, out and workspace 16 bytes; lse 4 bytes; rel_bias 2 bytes.
- * Limits: D = Dv in {16, 64, 128, 256}; sizes must keep every element count below 2^62.
+ * Limits: D = Dv in {16, 64, 128, 256}; Hkv * D <= 2^23; sizes must keep every element
+ * count below 2^62.
  */
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                        int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale,
