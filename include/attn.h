@@ -18,8 +18,8 @@
  *     multiple of 128, and the band rule d = i + (k_len - q_len) - j,
  *     score += rel_bias[cu_seqlens_q[b] + i, h, d] for 0 <= d < rel_extent.
  *   - "h3-blackwell-runtime" FLASH4.md, section API: native
- *     [batch, sequence, heads, head_dim] layout; a violated requirement raises
- *     an error instead of switching kernels (no fallback).
+ *     [batch, sequence, heads, head_dim] layout; an unmet requirement is an
+ *     error, never a reason to use another kernel (no fallback).
  *   - TabPFN issue "FlashAttention-4 backend for Blackwell" (#1235), closing
  *     comment: the returned LSE lets split-KV be merged outside the kernel.
  *
