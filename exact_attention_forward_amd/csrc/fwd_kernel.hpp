@@ -333,6 +333,8 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     };
     auto rescale_acc = [&]() __attribute__((always_inline)) {
         if (rescale_o) {
+            // keeps this rare block a real branch (not speculated into every tile)
+            asm volatile("; O rescale" ::: "memory");
 #pragma unroll
             for (int qb = 0; qb < T::NQB; qb++)
 #pragma unroll
@@ -361,7 +363,6 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
                 for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[qb][kb2][r]);
             m_run[qb] = fmaxf(m_run[qb], partner_max(mx) * p.c2);
         }
-        update_used_max();
     };
     auto exp_fast = [&](STile& s) __attribute__((always_inline)) {
 #pragma unroll
@@ -410,7 +411,6 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
                 }
             m_run[qb] = fmaxf(m_run[qb], partner_max(mx));
         }
-        update_used_max();
     };
     auto exp_slow = [&](STile& s) __attribute__((always_inline)) {
 #pragma unroll
@@ -468,41 +468,38 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
             if (!dv_ok) w = u32x4{0u, 0u, 0u, 0u};
             return __builtin_bit_cast(v8, w);
         };
+#pragma unroll
+        for (int t = 0; t < T::BN / 16; t++) {
+            v8 pt[T::NQB];
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++)
+#pragma unroll
+                for (int e = 0; e < 8; e++) pt[qb][e] = E::to_elem(s[qb][t >> 1][8 * (t & 1) + e]);
+#pragma unroll
+            for (int dt = 0; dt < T::NDT; dt++) {
+                const v8 a = vfrag(t, dt);
+#pragma unroll
+                for (int qb = 0; qb < T::NQB; qb++) o[qb][dt] = E::mma(a, pt[qb], o[qb][dt]);
+            }
+        }
         if (BF && any_lo) {
+            // rare: the remainder P - bf16(P) of the small-normaliser rows, accumulated in place
+            asm volatile("; P remainder" ::: "memory");
 #pragma unroll
             for (int t = 0; t < T::BN / 16; t++) {
-                v8 pt[T::NQB], ptl[T::NQB];
+                v8 ptl[T::NQB];
 #pragma unroll
                 for (int qb = 0; qb < T::NQB; qb++)
 #pragma unroll
                     for (int e = 0; e < 8; e++) {
                         const float pvv = s[qb][t >> 1][8 * (t & 1) + e];
-                        pt[qb][e] = E::to_elem(pvv);
-                        ptl[qb][e] = E::to_elem(need_lo[qb] ? pvv - (float)pt[qb][e] : 0.f);
+                        ptl[qb][e] = E::to_elem(need_lo[qb] ? pvv - (float)E::to_elem(pvv) : 0.f);
                     }
 #pragma unroll
                 for (int dt = 0; dt < T::NDT; dt++) {
                     const v8 a = vfrag(t, dt);
 #pragma unroll
-                    for (int qb = 0; qb < T::NQB; qb++) {
-                        o[qb][dt] = E::mma(a, pt[qb], o[qb][dt]);
-                        o[qb][dt] = E::mma(a, ptl[qb], o[qb][dt]);
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < T::BN / 16; t++) {
-                v8 pt[T::NQB];
-#pragma unroll
-                for (int qb = 0; qb < T::NQB; qb++)
-#pragma unroll
-                    for (int e = 0; e < 8; e++) pt[qb][e] = E::to_elem(s[qb][t >> 1][8 * (t & 1) + e]);
-#pragma unroll
-                for (int dt = 0; dt < T::NDT; dt++) {
-                    const v8 a = vfrag(t, dt);
-#pragma unroll
-                    for (int qb = 0; qb < T::NQB; qb++) o[qb][dt] = E::mma(a, pt[qb], o[qb][dt]);
+                    for (int qb = 0; qb < T::NQB; qb++) o[qb][dt] = E::mma(a, ptl[qb], o[qb][dt]);
                 }
             }
         }
@@ -543,15 +540,15 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
             const bool band = BIAS && (i_hi + delta - j0 >= 0) && (i_lo + delta - (j0 + T::BN - 1) < p.E);
             STile s;
             qk(kstage(r % T::NB), s);
-            if (!need_mask && !band && p.c2 > 0.f) {
-                max_fast(s);
-                rescale_acc();
-                exp_fast(s);
-            } else {
-                max_slow(s, j0, band);
-                rescale_acc();
-                exp_slow(s);
-            }
+            // O is only touched in straight-line code (the rescale and PV), so the
+            // fast / slow branches merge no accumulator state
+            const bool fast = !need_mask && !band && p.c2 > 0.f;
+            if (fast) max_fast(s);
+            else max_slow(s, j0, band);
+            update_used_max();
+            rescale_acc();
+            if (fast) exp_fast(s);
+            else exp_slow(s);
             pv(vstage(r % T::NB), s);
             // tiles issued after kb+1: kb+2 .. min(kb+PREFETCH, kb_end-1)
             wait_tiles_after_next(min(kb + T::PREFETCH, kb_end - 1) - (kb + 1));
