@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
     const int l32 = lane & 31;
     const int hf = lane >> 5;
 
@@ -260,9 +260,14 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
 
     auto issue_tile = [&](const uint16_t* base, int kb, char* dst, bool is_v) __attribute__((always_inline)) {
         const int j0 = kb * T::BN;
-        const int rows = max(0, min(T::BN, k_len - j0));
+        // every field of the descriptor is wave-uniform; saying so keeps the loads
+        // free of the per-lane "waterfall" the compiler would otherwise wrap them in
+        const int nrec = __builtin_amdgcn_readfirstlane(max(0, min(T::BN, k_len - j0)) * row_bytes);
+        const uint64_t addr = (uint64_t)(base + (long long)j0 * p.Hkv * D);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(base + (long long)j0 * p.Hkv * D), (short)0, rows * row_bytes, 0x00020000);
+            (void*)(((uint64_t)hi << 32) | lo), (short)0, nrec, 0x00020000);
 #pragma unroll
         for (int u = 0; u < T::LOADS; u++) {
             const int g0 = T::NT * u + 64 * wave;  // first granule of this wave's instruction
@@ -522,37 +527,44 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
 #undef MI355_WAIT_VM
     };
     static_assert(T::PREFETCH == 3, "wait_tiles_after_next covers up to two later tiles");
-    auto issue = [&](int j) __attribute__((always_inline)) {
-        const int st = (j - kb_begin) % T::NB;
+    auto issue = [&](int j, int st) __attribute__((always_inline)) {
         issue_tile(kbase, j, kstage(st), false);
         issue_tile(vbase, j, vstage(st), true);
     };
+    // one key tile; st = (kb - kb_begin) % NB is a literal at every call site, so all
+    // LDS addresses are a per-lane base plus an immediate offset
+    auto tile_step = [&](int kb, int st) __attribute__((always_inline)) {
+        if (kb + T::PREFETCH < kb_end) issue(kb + T::PREFETCH, (st + T::PREFETCH) % T::NB);
+        const int j0 = kb * T::BN;
+        const bool need_mask = (j0 + T::BN > k_len) || (CAUSAL && (j0 + T::BN - 1 > i_lo + delta));
+        const bool band = BIAS && (i_hi + delta - j0 >= 0) && (i_lo + delta - (j0 + T::BN - 1) < p.E);
+        STile s;
+        qk(kstage(st), s);
+        // O is only touched in straight-line code (the rescale and PV), so the
+        // fast / slow branches merge no accumulator state
+        const bool fast = !need_mask && !band && p.c2 > 0.f;
+        if (fast) max_fast(s);
+        else max_slow(s, j0, band);
+        update_used_max();
+        rescale_acc();
+        if (fast) exp_fast(s);
+        else exp_slow(s);
+        pv(vstage(st), s);
+        // tiles issued after kb+1: kb+2 .. min(kb+PREFETCH, kb_end-1)
+        wait_tiles_after_next(min(kb + T::PREFETCH, kb_end - 1) - (kb + 1));
+        __syncthreads();
+    };
+    static_assert(T::NB == 4, "the tile loop is unrolled over the four ring stages");
     if (kb_begin < kb_end) {
         const int first_end = min(kb_begin + T::PREFETCH, kb_end);
-        for (int j = kb_begin; j < first_end; j++) issue(j);
+        for (int j = kb_begin; j < first_end; j++) issue(j, j - kb_begin);
         wait_tiles_after_next(first_end - 1 - kb_begin);  // tile kb_begin has landed
         __syncthreads();
-        for (int kb = kb_begin; kb < kb_end; kb++) {
-            const int r = kb - kb_begin;
-            if (kb + T::PREFETCH < kb_end) issue(kb + T::PREFETCH);
-            const int j0 = kb * T::BN;
-            const bool need_mask = (j0 + T::BN > k_len) || (CAUSAL && (j0 + T::BN - 1 > i_lo + delta));
-            const bool band = BIAS && (i_hi + delta - j0 >= 0) && (i_lo + delta - (j0 + T::BN - 1) < p.E);
-            STile s;
-            qk(kstage(r % T::NB), s);
-            // O is only touched in straight-line code (the rescale and PV), so the
-            // fast / slow branches merge no accumulator state
-            const bool fast = !need_mask && !band && p.c2 > 0.f;
-            if (fast) max_fast(s);
-            else max_slow(s, j0, band);
-            update_used_max();
-            rescale_acc();
-            if (fast) exp_fast(s);
-            else exp_slow(s);
-            pv(vstage(r % T::NB), s);
-            // tiles issued after kb+1: kb+2 .. min(kb+PREFETCH, kb_end-1)
-            wait_tiles_after_next(min(kb + T::PREFETCH, kb_end - 1) - (kb + 1));
-            __syncthreads();
+        for (int kb = kb_begin; kb < kb_end; kb += T::NB) {
+            tile_step(kb, 0);
+            if (kb + 1 < kb_end) tile_step(kb + 1, 1);
+            if (kb + 2 < kb_end) tile_step(kb + 2, 2);
+            if (kb + 3 < kb_end) tile_step(kb + 3, 3);
         }
     }
 
