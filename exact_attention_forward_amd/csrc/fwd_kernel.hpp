@@ -389,44 +389,54 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     // Tiles that cross the key bound, the causal diagonal or the bias band (or scale <= 0).
     // Per element the arithmetic is the fast path's (one FMA into exp2, with the
     // bias term folded into the addend), so the result of a row does not depend on
-    // which path a tile takes; masked keys get p = 0. Phase 1 leaves the bias term
-    // (times log2 e) in s for visible keys and -inf for masked ones; phase 2
-    // recomputes s * c2 from the MFMA result kept in sraw.
-    float bt[T::NQB][T::NKB][16];
+    // which path a tile takes; masked keys get p = 0. The mask and the bias term
+    // are evaluated again in phase 2 (the bias row is then in cache) rather than
+    // kept in registers across the rescale.
+    auto slow_term = [&](int qb, int kb2, int r, int j0, bool band, const uint16_t* brow)
+        __attribute__((always_inline)) {
+        const int i = qi[qb];
+        const int j = j0 + kb2 * 32 + acc_row(r, hf);
+        const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
+        float b2 = 0.f;
+        if (BIAS && band) {
+            const int d = i + delta - j;
+            if (vis && qvalid[qb] && d >= 0 && d < p.E) b2 = E::widen(brow[d]) * kLog2e;
+        }
+        return vis ? b2 : -INFINITY;  // -inf marks a masked key
+    };
+    auto bias_row = [&](int qb) __attribute__((always_inline)) {
+        return BIAS ? p.bias + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)p.E : nullptr;
+    };
     auto max_slow = [&](STile& s, int j0, bool band) __attribute__((always_inline)) {
+        // opaque copy: keeps the per-element key indices inside the slow path
+        // instead of letting them be hoisted onto the fast path
+        asm volatile("" : "+s"(j0));
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
             float mx = -INFINITY;
-            const int i = qi[qb];
-            const uint16_t* brow = nullptr;
-            if (BIAS) brow = p.bias + ((q_off + i) * p.Hq + qh[qb]) * (long long)p.E;
+            const uint16_t* brow = bias_row(qb);
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const int j = j0 + kb2 * 32 + acc_row(r, hf);
-                    const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
-                    float b2 = 0.f;
-                    if (BIAS && band) {
-                        const int d = i + delta - j;
-                        if (vis && qvalid[qb] && d >= 0 && d < p.E) b2 = E::widen(brow[d]) * kLog2e;
-                    }
-                    bt[qb][kb2][r] = vis ? b2 : -INFINITY;
-                    mx = fmaxf(mx, vis ? __builtin_fmaf(s[qb][kb2][r], p.c2, b2) : -INFINITY);
+                    const float b2 = slow_term(qb, kb2, r, j0, band, brow);
+                    mx = fmaxf(mx, b2 == -INFINITY ? -INFINITY : __builtin_fmaf(s[qb][kb2][r], p.c2, b2));
                 }
             m_run[qb] = fmaxf(m_run[qb], partner_max(mx));
         }
     };
-    auto exp_slow = [&](STile& s) __attribute__((always_inline)) {
+    auto exp_slow = [&](STile& s, int j0, bool band) __attribute__((always_inline)) {
+        asm volatile("" : "+s"(j0));
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
             const float mu = m_used[qb] == -INFINITY ? 0.f : m_used[qb];
+            const uint16_t* brow = bias_row(qb);
             float rs = 0.f;
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const float b2 = bt[qb][kb2][r];
+                    const float b2 = slow_term(qb, kb2, r, j0, band, brow);
                     const float pv = b2 == -INFINITY ? 0.f
                                                      : __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, b2 - mu));
                     s[qb][kb2][r] = pv;
@@ -548,7 +558,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         update_used_max();
         rescale_acc();
         if (fast) exp_fast(s);
-        else exp_slow(s);
+        else exp_slow(s, j0, band);
         pv(vstage(st), s);
         // tiles issued after kb+1: kb+2 .. min(kb+PREFETCH, kb_end-1)
         wait_tiles_after_next(min(kb + T::PREFETCH, kb_end - 1) - (kb + 1));
