@@ -12,15 +12,18 @@
 // gfx950 mapping (one work-group = 4 waves; a wave owns NQB blocks of 32 rows):
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16}: A = a K row per lane
 //     (read from LDS, 16 bytes), B = the wave's Q rows, kept in registers.
-//     Lane l then holds 16 keys of query row l%32; lanes l and l^32 share a
-//     row, so a row max is an in-lane max plus one permlane32_swap.
+//     Per 32-key block, lane l then holds 16 keys of query row l%32; lanes l
+//     and l^32 share a row, so a row max is an in-lane max plus one
+//     permlane32_swap.
 //   * O^T = V^T P^T on the same MFMA: B = P^T comes straight from the S^T
 //     accumulators (same lane = same query), A = V^T is read from LDS with
 //     ds_read_b64_tr_b16 out of a 4x4-blocked V layout, so each 16-lane group
 //     reads 128 contiguous bytes. Every O^T register of a lane belongs to one
 //     query, so the online-softmax rescale is a per-lane scalar multiply.
-//   * K/V tiles of BN keys are double-buffered in LDS; global loads of tile
-//     t+1 are in flight while tile t is computed; one barrier per tile.
+//   * K/V tiles of BN keys (64 up to head dim 128, 32 at 256) sit in an LDS
+//     ring of PREFETCH + 1 stages (2 stages up to head dim 128, 4 at 256); the
+//     loads of the next PREFETCH tiles are in flight while a tile is computed;
+//     one barrier per tile.
 //   * Only tiles that cross the key bound, the causal diagonal or the bias band
 //     run the per-element mask / bias code.
 #pragma once
@@ -94,7 +97,7 @@ struct Tile {
     static constexpr int NG = D / 8;              // 16-byte granules per K / V row
     static constexpr int SWZ_DIV = NG >= 16 ? 1 : 16 / NG;
     static constexpr int TILE_BYTES = BN * D * 2; // one K or V tile in LDS
-    static constexpr int PREFETCH = 3;            // tiles loaded ahead of the one being consumed
+    static constexpr int PREFETCH = tile_prefetch(D);  // tiles loaded ahead of the one being consumed
     static constexpr int NB = PREFETCH + 1;       // LDS ring stages, each a K tile and a V tile
     // Two independent work-groups per CU for D <= 128 (each wave then fits in 256
     // registers and the SIMD interleaves one group's MFMAs with the other's softmax);
@@ -106,6 +109,7 @@ struct Tile {
     static constexpr int VM_PER_TILE = 2 * LOADS;           // buffer loads a wave issues per tile
     static_assert(D == 16 || D == 64 || D == 128 || D == 256, "head dim");
     static_assert(LDS * WG_PER_CU <= 160 * 1024, "LDS budget");
+    static_assert(NB <= 4, "tile loop unrolled over at most four ring stages");
     static_assert(GRANULES % 64 == 0, "whole waves per load instruction");
 };
 
@@ -531,12 +535,12 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         constexpr int L = T::VM_PER_TILE;
         static_assert((T::PREFETCH - 1) * L < 64, "vmcnt field");
 #define MI355_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
-        if (n_after <= 0) MI355_WAIT_VM(0);
-        else if (n_after == 1) MI355_WAIT_VM(L);
+        if (T::PREFETCH <= 1 || n_after <= 0) MI355_WAIT_VM(0);
+        else if (T::PREFETCH == 2 || n_after == 1) MI355_WAIT_VM(L);
         else MI355_WAIT_VM(2 * L);
 #undef MI355_WAIT_VM
     };
-    static_assert(T::PREFETCH == 3, "wait_tiles_after_next covers up to two later tiles");
+    static_assert(T::PREFETCH >= 1 && T::PREFETCH <= 3, "wait_tiles_after_next covers up to two later tiles");
     auto issue = [&](int j, int st) __attribute__((always_inline)) {
         issue_tile(kbase, j, kstage(st), false);
         issue_tile(vbase, j, vstage(st), true);
@@ -564,17 +568,17 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         wait_tiles_after_next(min(kb + T::PREFETCH, kb_end - 1) - (kb + 1));
         __syncthreads();
     };
-    static_assert(T::NB == 4, "the tile loop is unrolled over the four ring stages");
     if (kb_begin < kb_end) {
         const int first_end = min(kb_begin + T::PREFETCH, kb_end);
         for (int j = kb_begin; j < first_end; j++) issue(j, j - kb_begin);
         wait_tiles_after_next(first_end - 1 - kb_begin);  // tile kb_begin has landed
         __syncthreads();
+        // unrolled over the ring stages (NB <= 4)
         for (int kb = kb_begin; kb < kb_end; kb += T::NB) {
             tile_step(kb, 0);
-            if (kb + 1 < kb_end) tile_step(kb + 1, 1);
-            if (kb + 2 < kb_end) tile_step(kb + 2, 2);
-            if (kb + 3 < kb_end) tile_step(kb + 3, 3);
+            if (T::NB > 1 && kb + 1 < kb_end) tile_step(kb + 1, 1 % T::NB);
+            if (T::NB > 2 && kb + 2 < kb_end) tile_step(kb + 2, 2 % T::NB);
+            if (T::NB > 3 && kb + 3 < kb_end) tile_step(kb + 3, 3 % T::NB);
         }
     }
 

@@ -16,7 +16,9 @@ struct TileGeom {
 
 __host__ __device__ constexpr int tile_nqb(int /*D*/) { return 1; }
 __host__ __device__ constexpr int tile_bm(int D) { return 4 * 32 * tile_nqb(D); }
-__host__ __device__ constexpr int tile_bn(int /*D*/) { return 32; }
+__host__ __device__ constexpr int tile_bn(int D) { return D <= 128 ? 64 : 32; }
+// K/V tiles loaded ahead of the one being consumed (the LDS ring has one more stage)
+__host__ __device__ constexpr int tile_prefetch(int D) { return D <= 128 ? 1 : 3; }
 
 struct FwdParams {
     const uint16_t* q;

@@ -121,34 +121,40 @@ def test_workspace_and_splits(lib):
     assert check(lib, ns=4, Sk=100000, ws=A + 4, ws_bytes=need) == CODE["ATTN_ERR_MISALIGNED"]
     assert lib.attn_fwd_workspace_size(1, 257, 8, 128, 0, 1) == 0
     # requested splits are clamped to the number of key blocks and to 256
-    assert lib.attn_num_splits(1, 10, 200, 1, 1, 64, 64, 0, 0, 0, -1, 50) == ceil_div(200, BN)
+    assert lib.attn_num_splits(1, 10, 200, 1, 1, 64, 64, 0, 0, 0, -1, 50) == ceil_div(200, bn(64))
     assert lib.attn_num_splits(1, 10, 10**6, 1, 1, 64, 64, 0, 0, 0, -1, 1000) == 256
     # heuristic: no split when the grid already covers the 256 compute units
     assert lib.attn_num_splits(1, 20480, 20480, 56, 56, 128, 128, 0, 0, 0, -1, 0) == 1
     # decode B=32, one KV head, 8:1 packed into one row tile: 32 work-groups
-    assert lib.attn_num_splits(32, 1, 131072, 8, 1, 256, 256, 0, 0, 0, -1, 0) == heuristic(32, 131072)
+    assert lib.attn_num_splits(32, 1, 131072, 8, 1, 256, 256, 0, 0, 0, -1, 0) == heuristic(32, 131072, 256)
     # short query, long keys: 6 heads x ceil(1000 / BM) row tiles
     wg = 6 * ceil_div(1000, BM)
-    assert lib.attn_num_splits(1, 1000, 10**6, 6, 6, 64, 64, 0, 0, 0, -1, 0) == heuristic(wg, 10**6)
+    assert lib.attn_num_splits(1, 1000, 10**6, 6, 6, 64, 64, 0, 0, 0, -1, 0) == heuristic(wg, 10**6, 64)
     # never fewer than 4 key blocks per split
-    assert lib.attn_num_splits(1, 1, 640, 1, 1, 64, 64, 0, 0, 0, -1, 0) == ceil_div(640, BN) // 4
+    assert lib.attn_num_splits(1, 1, 640, 1, 1, 64, 64, 0, 0, 0, -1, 0) == ceil_div(640, bn(64)) // 4
+    assert lib.attn_num_splits(1, 1, 640, 1, 1, 256, 256, 0, 0, 0, -1, 0) == ceil_div(640, bn(256)) // 4
     # varlen sizes come from max_seqlen
     assert lib.attn_num_splits(4, 400, 400000, 8, 8, 128, 128, 1, 100, 100000, -1, 0) == \
-        heuristic(4 * 8 * ceil_div(100, BM), 100000)
+        heuristic(4 * 8 * ceil_div(100, BM), 100000, 128)
 
 
-BM, BN = 128, 32  # rows per work-group and keys per key block of the forward kernel
+BM = 128  # rows per work-group of the forward kernel
+
+
+def bn(D):
+    """Keys per key block of the forward kernel: 64 up to head dim 128, 32 at 256."""
+    return 64 if D <= 128 else 32
 
 
 def ceil_div(a, b):
     return -(-a // b)
 
 
-def heuristic(work_groups, k_len):
+def heuristic(work_groups, k_len, D):
     """The documented split rule: floor(256 / work-groups), at least 4 key blocks per split."""
     if work_groups >= 256:
         return 1
-    return max(1, min(256 // work_groups, max(1, ceil_div(k_len, BN) // 4), 256))
+    return max(1, min(256 // work_groups, max(1, ceil_div(k_len, bn(D)) // 4), 256))
 
 
 def test_python_binding_rejects_bad_dtype():
