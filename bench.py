@@ -118,6 +118,66 @@ def read_traffic(workload, dtype):
         return None
 
 
+COPY_BYTES = 1 << 30  # bytes read and written by each calibration copy
+
+
+def counter_means(run_dir, counter):
+    """Per-dispatch values of one counter from a rocprofv3 --pmc run: (attention fwd, copies)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {run_dir}, found {files}")
+    fwd, other = [], []
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0  # the counter is in KiB
+            (fwd if "attn_fwd_kernel" in r["Kernel_Name"] else other).append(
+                (v, r["Kernel_Name"]))
+    # the calibration copies are the three elementwise launches that move the most bytes
+    copies = sorted(v for v, name in other if "elementwise" in name)[-3:]
+    if not fwd or len(copies) != 3:
+        raise SystemExit(f"{run_dir}: {len(fwd)} forward dispatches, {len(copies)} copies")
+    return [v for v, _ in fwd], copies
+
+
+def write_traffic(args, fetch_dir, write_dir):
+    """profiles/traffic_<workload>_<dtype>.txt from a FETCH_SIZE run and a WRITE_SIZE run.
+
+    Each counter is scaled by the ratio of the bytes a plain 1 GiB copy moves to what
+    the same counter reads for it, so the figure is HBM-side bytes per forward launch.
+    """
+    from workloads import configs
+    spec = configs.workload(args.workload, args.dtype)
+    f_fwd, f_copy = counter_means(fetch_dir, "FETCH_SIZE")
+    w_fwd, w_copy = counter_means(write_dir, "WRITE_SIZE")
+    f_scale = COPY_BYTES / float(np.mean(f_copy))
+    w_scale = COPY_BYTES / float(np.mean(w_copy))
+    fetch = float(np.mean(f_fwd)) * f_scale
+    write = float(np.mean(w_fwd)) * w_scale
+    path = os.path.join(REPO, "profiles", f"traffic_{args.workload}_{spec.dtype}.txt")
+    cmd = (f"python -u bench.py --no-cpu --steps 3 --warmup 1 --workload {args.workload} "
+           f"--dtype {spec.dtype} --copy-calibration")
+    with open(path, "w") as f:
+        f.write(f"# HBM traffic of attn_fwd_kernel per launch, {args.workload} "
+                f"({DESCRIPTION[args.workload]}), {spec.dtype}\n")
+        f.write(f"# counters: rocprofv3 --pmc FETCH_SIZE -- {cmd}\n")
+        f.write(f"#           rocprofv3 --pmc WRITE_SIZE -- {cmd}\n")
+        f.write("# scale = bytes of a plain 1 GiB elementwise copy / what the counter reads for it\n")
+        f.write(f"fetch_dispatches = {len(f_fwd)}\n")
+        f.write(f"fetch_raw_bytes_per_launch = {np.mean(f_fwd):.0f}\n")
+        f.write(f"fetch_scale = {f_scale:.4f}\n")
+        f.write(f"write_raw_bytes_per_launch = {np.mean(w_fwd):.0f}\n")
+        f.write(f"write_scale = {w_scale:.4f}\n")
+        f.write(f"fetch_bytes_per_launch = {fetch:.0f}\n")
+        f.write(f"write_bytes_per_launch = {write:.0f}\n")
+        f.write(f"hbm_bytes_per_launch = {fetch + write:.0f}\n")
+        f.write(f"kernel_source_hash = {kernel_source_hash()}\n")
+    print(open(path).read())
+
+
 def sample_rows(spec, x, n, seed=12345):
     """Deterministic sample of (b, h, i) rows spread over batches, heads and positions."""
     from workloads import gen
@@ -193,9 +253,16 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB elementwise copy (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: turn the counter CSVs of two rocprofv3 --pmc runs of "
+                         "bench.py --copy-calibration (FETCH_SIZE, then WRITE_SIZE) into "
+                         "profiles/traffic_<workload>_<dtype>.txt")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(args, *args.traffic_from)
+        return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the path would "
+        print(f"bench.py: measures one GPU only (asked for {args.gpus}); the path would "
               "shard over (batch, KV head) with no exchange, or over the key range with one "
               "LSE combine step", file=sys.stderr)
         sys.exit(2)
