@@ -17,9 +17,14 @@ LIB = os.path.join(HERE, "libmi355attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated (see the design notes)
+# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated; some of their forms
+#   have given wrong results on gfx950 now and then, with no error
+# max-ilp scheduling: LDS operands are read well ahead of the MFMAs that use them
+#   (the default strategy trades that latency hiding for registers the kernels do
+#   not need at their occupancy)
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-sched-strategy=max-ilp",
           "-I" + os.path.join(os.path.dirname(HERE), "include")]
 
 

@@ -103,10 +103,6 @@ struct Tile {
     // registers and the SIMD interleaves one group's MFMAs with the other's softmax);
     // at D = 256 a wave needs more than 256 registers, so one group per CU.
     static constexpr int WG_PER_CU = D <= 128 ? 2 : 1;
-    // Software-pipelined tile loop (S of the next tile on the MFMAs while the
-    // VALU works on the current one) where the doubled score tile fits the
-    // 256-register budget of two work-groups per CU.
-    static constexpr bool PIPE = false;
     static constexpr int LDS = NB * 2 * TILE_BYTES;
     static constexpr int GRANULES = BN * NG;      // 16-byte granules per tile
     static constexpr int LOADS = (GRANULES + NT - 1) / NT;  // per thread, per K (or V) tile
@@ -114,7 +110,6 @@ struct Tile {
     static_assert(D == 16 || D == 64 || D == 128 || D == 256, "head dim");
     static_assert(LDS * WG_PER_CU <= 160 * 1024, "LDS budget");
     static_assert(NB <= 4, "tile loop unrolled over at most four ring stages");
-    static_assert(!PIPE || NB == 2, "the pipelined loop keeps two ring stages");
     static_assert(GRANULES % NT == 0 || LOADS == 1, "a wave issues all of its loads of a tile or none");
     static_assert(GRANULES % 64 == 0, "whole waves per load instruction");
 };
@@ -157,20 +152,6 @@ __device__ __forceinline__ void wait_vm_loads() {
 }
 __device__ __forceinline__ void wait_vm_all() { wait_vm_loads<0>(); }
 
-// Scheduling recipe for a block of N_MFMA MFMAs and independent VALU work:
-// LDS reads DS_AHEAD fragments ahead, then per MFMA: the MFMA, VALU_PER VALU
-// (transcendental included) instructions, DS_PER LDS reads. The VALU work
-// then issues in the shadow of the MFMAs instead of after them.
-template <int N_MFMA, int VALU_PER, int DS_PER, int DS_AHEAD>
-__device__ __forceinline__ void interleave_mfma_valu() {
-    if (DS_AHEAD > 0) __builtin_amdgcn_sched_group_barrier(0x100, DS_AHEAD, 0);
-#pragma unroll
-    for (int i = 0; i < N_MFMA; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, VALU_PER, 0);
-        if (DS_PER > 0) __builtin_amdgcn_sched_group_barrier(0x100, DS_PER, 0);
-    }
-}
 
 template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT>
 __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const FwdParams p) {
@@ -342,37 +323,18 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
 #pragma unroll
         for (int kb2 = 0; kb2 < T::NKB; kb2++) {
             const int key = kb2 * 32 + l32;
+            // all reads of a 32-key block go out before its MFMAs (the compiler
+            // barrier keeps them from being sunk back to their uses), so each MFMA
+            // finds its operand landed instead of waiting out the LDS latency
+            v8 ka[T::NC];
 #pragma unroll
-            for (int c = 0; c < T::NC; c++) {
-                const v8 a = *(const v8*)(kl + k_granule<D>(key, 2 * c + hf) * 16);
+            for (int c = 0; c < T::NC; c++) ka[c] = *(const v8*)(kl + k_granule<D>(key, 2 * c + hf) * 16);
+            asm volatile("" ::: "memory");
 #pragma unroll
-                for (int qb = 0; qb < T::NQB; qb++) s[qb][kb2] = E::mma(a, qf[qb][c], s[qb][kb2]);
-            }
+            for (int c = 0; c < T::NC; c++)
+#pragma unroll
+                for (int qb = 0; qb < T::NQB; qb++) s[qb][kb2] = E::mma(ka[c], qf[qb][c], s[qb][kb2]);
         }
-    };
-
-    // K fragments (A operand of S^T = K Q^T) of a whole tile, and the product from them
-    typedef v8 KFrags[T::NKB][T::NC];
-    auto load_kfrags = [&](const char* kl, KFrags& kf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < T::NKB; kb2++)
-#pragma unroll
-            for (int c = 0; c < T::NC; c++)
-                kf[kb2][c] = *(const v8*)(kl + k_granule<D>(kb2 * 32 + l32, 2 * c + hf) * 16);
-    };
-    auto qk_frags = [&](const KFrags& kf, STile& s) __attribute__((always_inline)) {
-#pragma unroll
-        for (int qb = 0; qb < T::NQB; qb++)
-#pragma unroll
-            for (int kb2 = 0; kb2 < T::NKB; kb2++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) s[qb][kb2][r] = 0.f;
-#pragma unroll
-        for (int kb2 = 0; kb2 < T::NKB; kb2++)
-#pragma unroll
-            for (int c = 0; c < T::NC; c++)
-#pragma unroll
-                for (int qb = 0; qb < T::NQB; qb++) s[qb][kb2] = E::mma(kf[kb2][c], qf[qb][c], s[qb][kb2]);
     };
 
     auto partner_max = [](float x) __attribute__((always_inline)) {
@@ -440,8 +402,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     auto exp_fast = [&](STile& s) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
-            // a row with nothing visible yet (its masked scores are -inf) refers to 0
-            const float mu = m_used[qb] == -INFINITY ? 0.f : m_used[qb];
+            const float mu = m_used[qb];
             float rs = 0.f;
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
@@ -472,21 +433,6 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
             if (vis && qvalid[qb] && d >= 0 && d < p.E) b2 = E::widen(brow[d]) * kLog2e;
         }
         return vis ? b2 : -INFINITY;  // -inf marks a masked key
-    };
-    // Masked tile without bias (positive scale): masked scores become -inf, after
-    // which the fast max and exp give exactly the slow path's values (p = 0 there).
-    auto mask_scores = [&](STile& s, int j0) __attribute__((always_inline)) {
-        asm volatile("" : "+s"(j0));
-#pragma unroll
-        for (int qb = 0; qb < T::NQB; qb++)
-#pragma unroll
-            for (int kb2 = 0; kb2 < T::NKB; kb2++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int j = j0 + kb2 * 32 + acc_row(r, hf);
-                    const bool vis = (j < k_len) && (!CAUSAL || j <= qi[qb] + delta);
-                    if (!vis) s[qb][kb2][r] = -INFINITY;
-                }
     };
     auto bias_row = [&](int qb) __attribute__((always_inline)) {
         return BIAS ? p.bias + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)p.E : nullptr;
@@ -572,54 +518,12 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         if (!dv_ok) w = u32x4{0u, 0u, 0u, 0u};
         return __builtin_bit_cast(v8, w);
     };
-    typedef v8 VFrags[T::BN / 16][T::NDT];
-    auto load_vfrags = [&](const char* vl, VFrags& vf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int t = 0; t < T::BN / 16; t++)
-#pragma unroll
-            for (int dt = 0; dt < T::NDT; dt++) vf[t][dt] = vfrag(vl, t, dt);
-    };
-    // O^T += V^T P^T, 16 keys per MFMA step, from V^T fragments already in registers.
-    // bf16 P carries a 2^-9 relative rounding error; for a row whose normaliser is
-    // still small (few keys hold its weight) that error can reach the output
-    // tolerance, so such rows also feed the remainder P - bf16(P) through a second
-    // MFMA. A row with normaliser l (max weight 1) has at least l effective keys,
-    // and the error shrinks like 2^-9 / sqrt(3 l); rows at or above kLoThresh skip it.
-    auto pv_frags = [&](const VFrags& vf, STile& s) __attribute__((always_inline)) {
-#pragma unroll
-        for (int t = 0; t < T::BN / 16; t++) {
-            v8 pt[T::NQB];
-#pragma unroll
-            for (int qb = 0; qb < T::NQB; qb++)
-#pragma unroll
-                for (int e = 0; e < 8; e++) pt[qb][e] = E::to_elem(s[qb][t >> 1][8 * (t & 1) + e]);
-#pragma unroll
-            for (int dt = 0; dt < T::NDT; dt++)
-#pragma unroll
-                for (int qb = 0; qb < T::NQB; qb++) o[qb][dt] = E::mma(vf[t][dt], pt[qb], o[qb][dt]);
-        }
-        if (BF && any_lo) {
-            // rare: the remainder P - bf16(P) of the small-normaliser rows, accumulated in place
-            asm volatile("; P remainder" ::: "memory");
-#pragma unroll
-            for (int t = 0; t < T::BN / 16; t++) {
-                v8 ptl[T::NQB];
-#pragma unroll
-                for (int qb = 0; qb < T::NQB; qb++)
-#pragma unroll
-                    for (int e = 0; e < 8; e++) {
-                        const float pvv = s[qb][t >> 1][8 * (t & 1) + e];
-                        ptl[qb][e] = E::to_elem(need_lo[qb] ? pvv - (float)E::to_elem(pvv) : 0.f);
-                    }
-#pragma unroll
-                for (int dt = 0; dt < T::NDT; dt++)
-#pragma unroll
-                    for (int qb = 0; qb < T::NQB; qb++) o[qb][dt] = E::mma(vf[t][dt], ptl[qb], o[qb][dt]);
-            }
-        }
-    };
-    // the same with the fragments read from LDS step by step (the register budget
-    // of the unpipelined loop has no room for a whole tile of them)
+    // O^T += V^T P^T, 16 keys per MFMA step. bf16 P carries a 2^-9 relative
+    // rounding error; for a row whose normaliser is still small (few keys hold
+    // its weight) that error can reach the output tolerance, so such rows also
+    // feed the remainder P - bf16(P) through a second MFMA. A row with
+    // normaliser l (max weight 1) has at least l effective keys, and the error
+    // shrinks like 2^-9 / sqrt(3 l); rows at or above kLoThresh skip it.
     auto pv = [&](const char* vl, STile& s) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < T::BN / 16; t++) {
@@ -636,6 +540,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
             }
         }
         if (BF && any_lo) {
+            // rare: the remainder P - bf16(P) of the small-normaliser rows, accumulated in place
             asm volatile("; P remainder" ::: "memory");
 #pragma unroll
             for (int t = 0; t < T::BN / 16; t++) {
@@ -702,109 +607,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         wait_tiles_after_next(min(kb + T::PREFETCH, kb_end - 1) - (kb + 1));
         __syncthreads();
     };
-    if constexpr (T::PIPE) {
-        // Software pipeline over key tiles inside each wave. Iteration kb first reads
-        // all of its LDS operands into registers (K(kb+1) and V(kb) fragments), which
-        // frees the ring stages read in the previous iteration, and refills them with
-        // K(kb+2) and V(kb+1) while it computes. Then the MFMAs of S(kb+1) = K Q^T run
-        // while the VALU turns S(kb) into P(kb), and the MFMAs of O^T += V^T P(kb)^T
-        // run while the row maxima of S(kb+1) are taken. Each wave waits for its own
-        // loads at the end of the iteration, and one barrier publishes them.
-        auto issue_k = [&](int j, int st) __attribute__((always_inline)) {
-            issue_tile(kbase, j, kstage(st), false);
-        };
-        auto issue_v = [&](int j, int st) __attribute__((always_inline)) {
-            issue_tile(vbase, j, vstage(st), true);
-        };
-        // Per tile and wave: masked (key bound or causal diagonal) and slow (bias
-        // band, or a scale <= 0). Masked tiles get their scores masked in place and
-        // then take the fast max / exp; slow tiles run the per-element slow path.
-        auto classify = [&](int kb, bool& masked, bool& band) __attribute__((always_inline)) {
-            const int j0 = kb * T::BN;
-            masked = (j0 + T::BN > k_len) || (CAUSAL && (j0 + T::BN - 1 > wi_lo + delta));
-            band = BIAS && (wi_hi + delta - j0 >= 0) && (wi_lo + delta - (j0 + T::BN - 1) < p.E);
-            return band || !(p.c2 > 0.f);
-        };
-        auto iter = [&](int kb, int st, STile& cur, STile& nxt) __attribute__((always_inline)) {
-            const bool has_next = kb + 1 < kb_end;
-            KFrags kf;
-            VFrags vf;
-            if (has_next) load_kfrags(kstage(st ^ 1), kf);
-            load_vfrags(vstage(st), vf);
-            if (kb + 2 < kb_end) issue_k(kb + 2, st);      // K(kb) was read last iteration
-            if (kb + 1 < kb_end) issue_v(kb + 1, st ^ 1);  // and V(kb-1)
-            const int j0 = kb * T::BN;
-            bool masked, band;
-            const bool slow = classify(kb, masked, band);
-            // S(kb+1) on the MFMAs while P(kb) is formed; the markers keep the compiler
-            // from hoisting the shared MFMAs out of the two versions
-            if (has_next) {
-                if (!slow) {
-                    asm volatile("; stage A" ::: "memory");
-                    qk_frags(kf, nxt);
-                    exp_fast(cur);
-                    interleave_mfma_valu<T::NKB * T::NC, 7, 0, 0>();
-                } else {
-                    asm volatile("; stage A slow" ::: "memory");
-                    qk_frags(kf, nxt);
-                    exp_slow(cur, j0, band);
-                }
-            } else {
-                if (!slow) exp_fast(cur);
-                else exp_slow(cur, j0, band);
-            }
-            lo_decision();
-            // O += V(kb) P(kb) on the MFMAs while the row maxima of S(kb+1) are taken
-            if (has_next) {
-                bool masked1, band1;
-                const bool slow1 = classify(kb + 1, masked1, band1);
-                if (!slow1) {
-                    if (masked1) mask_scores(nxt, j0 + T::BN);
-                    asm volatile("; stage B" ::: "memory");
-                    pv_frags(vf, cur);
-                    max_fast(nxt);
-                    interleave_mfma_valu<T::NDT * T::BN / 16, 4, 0, 0>();
-                } else {
-                    asm volatile("; stage B slow" ::: "memory");
-                    pv_frags(vf, cur);
-                    max_slow(nxt, j0 + T::BN, band1);
-                }
-                update_used_max();
-                rescale_acc();  // O now holds tile kb: bring it to the new reference max
-            } else {
-                pv_frags(vf, cur);
-            }
-            wait_vm_all();
-            __syncthreads();
-        };
-        if (kb_begin < kb_end) {
-            STile sa, sb;
-            issue_k(kb_begin, 0);
-            issue_v(kb_begin, 0);
-            if (kb_begin + 1 < kb_end) issue_k(kb_begin + 1, 1);
-            wait_vm_all();
-            __syncthreads();
-            bool masked, band;
-            const bool slow = classify(kb_begin, masked, band);
-            {
-                KFrags kf;
-                load_kfrags(kstage(0), kf);
-                qk_frags(kf, sa);
-            }
-            if (slow) {
-                max_slow(sa, kb_begin * T::BN, band);
-            } else {
-                if (masked) mask_scores(sa, kb_begin * T::BN);
-                max_fast(sa);
-            }
-            update_used_max();  // O is still zero: nothing to rescale
-            __syncthreads();    // K(kb_begin) read by every wave before its stage is refilled
-            for (int kb = kb_begin; kb < kb_end; kb += 2) {
-                iter(kb, 0, sa, sb);
-                if (kb + 1 < kb_end) iter(kb + 1, 1, sb, sa);
-            }
-        }
-    } else if (kb_begin < kb_end) {
+    if (kb_begin < kb_end) {
         const int first_end = min(kb_begin + T::PREFETCH, kb_end);
         for (int j = kb_begin; j < first_end; j++) issue(j, j - kb_begin);
         wait_tiles_after_next(first_end - 1 - kb_begin);  // tile kb_begin has landed
