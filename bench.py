@@ -50,6 +50,9 @@ DESCRIPTION = {
     "c4c": "cross attention q[1,1000,6,64] k/v[1,1e6,6,64], split-KV heuristic",
     "c5a": "8:1 pack-GQA D256 q[4,1024,8,256] k/v[4,2048,1,256] seqused_k U[600,2048]",
     "c5b": "D256 decode q[32,1,8,256] k/v[32,131072,1,256] causal, split-KV + combine",
+    "n1a": "cached prediction fp16 MQA 8:1 D64, q[1,16,8,64] k/v[1,300000,1,64], split-KV",
+    "n1b": "cached prediction fp16 MQA 8:1 D64, q[1,64,8,64] k/v[1,300000,1,64], split-KV",
+    "n1c": "cached prediction fp16 MQA 8:1 D64, q[1,256,8,64] k/v[1,300000,1,64], split-KV",
 }
 
 
@@ -178,6 +181,32 @@ def write_traffic(args, fetch_dir, write_dir):
     print(open(path).read())
 
 
+def graph_timing(fa, q, k, v, kw, steps, eager_ms_step, kernel_ms):
+    """Microseconds per call: eager (the timed loop above), one call captured in a HIP
+    graph and replayed back to back, and the kernels alone (events)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fa.attn_fwd(q, k, v, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.attn_fwd(q, k, v, **kw)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) * 1e6 / steps
+    return {"eager_us_per_call": eager_ms_step * 1e3, "graph_us_per_call": graph_us,
+            "kernel_us_per_call": kernel_ms * 1e3}
+
+
 def sample_rows(spec, x, n, seed=12345):
     """Deterministic sample of (b, h, i) rows spread over batches, heads and positions."""
     from workloads import gen
@@ -251,6 +280,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the call captured in a HIP graph and replayed (host "
+                         "dispatch overhead: eager vs graph microseconds per call)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB elementwise copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -367,6 +399,9 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
     }
+    if args.graph:
+        result["dispatch"] = graph_timing(fa, q, k, v, kw, args.steps, ms_step, mean_call_ms)
+        log(f"dispatch: {result['dispatch']}")
     if not args.no_cpu:
         threads = min(16, os.cpu_count() or 1)
         cb, check = cpu_baseline(spec, x, out, lse, args.cpu_seconds, threads)

@@ -68,10 +68,11 @@ bool make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int is_varlen, int
         ns = num_splits;
         if (ns > pl.nkb_max) ns = pl.nkb_max;
         if (ns > ATTN_MAX_SPLITS) ns = ATTN_MAX_SPLITS;
-    } else if (base == 0 || base >= kNumCUs) {
+    } else if (base == 0 || base >= (long long)kNumCUs * tile_wg_per_cu(D)) {
         ns = 1;
     } else {
-        ns = (int)(kNumCUs / base);
+        // one wave of resident work-groups: CUs x work-groups per CU
+        ns = (int)((long long)kNumCUs * tile_wg_per_cu(D) / base);
         const int cap = pl.nkb_max / 4 > 0 ? pl.nkb_max / 4 : 1;
         if (ns > cap) ns = cap;
         if (ns > ATTN_MAX_SPLITS) ns = ATTN_MAX_SPLITS;

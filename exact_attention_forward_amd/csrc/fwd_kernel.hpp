@@ -99,10 +99,7 @@ struct Tile {
     static constexpr int TILE_BYTES = BN * D * 2; // one K or V tile in LDS
     static constexpr int PREFETCH = tile_prefetch(D);  // tiles loaded ahead of the one being consumed
     static constexpr int NB = PREFETCH + 1;       // LDS ring stages, each a K tile and a V tile
-    // Two independent work-groups per CU for D <= 128 (each wave then fits in 256
-    // registers and the SIMD interleaves one group's MFMAs with the other's softmax);
-    // at D = 256 a wave needs more than 256 registers, so one group per CU.
-    static constexpr int WG_PER_CU = D <= 128 ? 2 : 1;
+    static constexpr int WG_PER_CU = tile_wg_per_cu(D);
     static constexpr int LDS = NB * 2 * TILE_BYTES;
     static constexpr int GRANULES = BN * NG;      // 16-byte granules per tile
     static constexpr int LOADS = (GRANULES + NT - 1) / NT;  // per thread, per K (or V) tile

@@ -17,6 +17,9 @@ struct TileGeom {
 __host__ __device__ constexpr int tile_nqb(int /*D*/) { return 1; }
 __host__ __device__ constexpr int tile_bm(int D) { return 4 * 32 * tile_nqb(D); }
 __host__ __device__ constexpr int tile_bn(int D) { return D <= 128 ? 64 : 32; }
+// Work-groups resident per CU: two up to head dim 128; at 256 a wave needs more
+// than 256 registers, so one.
+__host__ __device__ constexpr int tile_wg_per_cu(int D) { return D <= 128 ? 2 : 1; }
 // K/V tiles loaded ahead of the one being consumed (the LDS ring has one more stage)
 __host__ __device__ constexpr int tile_prefetch(int D) { return D <= 128 ? 1 : 3; }
 

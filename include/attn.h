@@ -134,9 +134,11 @@ attn_status_t attn_check_args(const void* q, const void* k, const void* v, void*
  * sizes and this request (num_splits <= 0: the heuristic; otherwise the
  * request clamped). is_varlen selects the meaning of Sq/Sk as in attn_fwd.
  * Pure host function. Returns >= 1, or 0 for invalid sizes.
- * Heuristic: split only when the unsplit grid has fewer work-groups than the
- * 256 compute units; then use floor(256 / work-groups) splits (one wave of
- * work-groups fills the chip), never fewer than 4 key blocks per split.
+ * Heuristic: split only when the unsplit grid has fewer work-groups than fit
+ * on the chip at once (256 compute units x 2 work-groups each for D <= 128,
+ * x 1 for D = 256); then use floor(that / work-groups) splits (one wave of
+ * work-groups fills the chip), never fewer than 4 key blocks per split (64 keys
+ * per block for D <= 128, 32 for D = 256).
  */
 int attn_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_varlen,
                     int max_seqlen_q, int max_seqlen_k, int pack_gqa, int num_splits);

@@ -183,9 +183,10 @@ def random_case(rng_seed, *, dtype, B, Sq, Sk, Hq, Hkv, D, causal=False, varlen_
                 num_splits=num_splits, pack_gqa=pack_gqa, name=name)
 
 
-def full_check(case: Case, **over):
-    """GPU vs the full oracle; returns (O max err, LSE max err)."""
-    out, lse = case.run_gpu(**over)
+def full_check(case: Case, out_lse=None, **over):
+    """GPU vs the full oracle; returns (O max err, LSE max err). out_lse: results
+    already computed (else the case runs here)."""
+    out, lse = case.run_gpu(**over) if out_lse is None else out_lse
     O_ref, L_ref = case.oracle_full()
     o = host_f64(out, case.dtype)
     l = lse.cpu().numpy().astype(np.float64)

@@ -123,8 +123,10 @@ def test_workspace_and_splits(lib):
     # requested splits are clamped to the number of key blocks and to 256
     assert lib.attn_num_splits(1, 10, 200, 1, 1, 64, 64, 0, 0, 0, -1, 50) == ceil_div(200, bn(64))
     assert lib.attn_num_splits(1, 10, 10**6, 1, 1, 64, 64, 0, 0, 0, -1, 1000) == 256
-    # heuristic: no split when the grid already covers the 256 compute units
+    # heuristic: no split when the grid already covers the chip
     assert lib.attn_num_splits(1, 20480, 20480, 56, 56, 128, 128, 0, 0, 0, -1, 0) == 1
+    assert lib.attn_num_splits(1, 1024, 20480, 4, 4, 128, 128, 0, 0, 0, -1, 0) == heuristic(32, 20480, 128)
+    assert lib.attn_num_splits(1, 2048, 20480, 2, 1, 256, 256, 0, 0, 0, -1, 0) == heuristic(32, 20480, 256)
     # decode B=32, one KV head, 8:1 packed into one row tile: 32 work-groups
     assert lib.attn_num_splits(32, 1, 131072, 8, 1, 256, 256, 0, 0, 0, -1, 0) == heuristic(32, 131072, 256)
     # short query, long keys: 6 heads x ceil(1000 / BM) row tiles
@@ -150,11 +152,16 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
+def resident(D):
+    """Work-groups that fit on the chip at once: 256 CUs x 2 (D <= 128) or x 1 (D = 256)."""
+    return 256 * (2 if D <= 128 else 1)
+
+
 def heuristic(work_groups, k_len, D):
-    """The documented split rule: floor(256 / work-groups), at least 4 key blocks per split."""
-    if work_groups >= 256:
+    """The documented split rule: floor(resident / work-groups), at least 4 key blocks per split."""
+    if work_groups >= resident(D):
         return 1
-    return max(1, min(256 // work_groups, max(1, ceil_div(k_len, bn(D)) // 4), 256))
+    return max(1, min(resident(D) // work_groups, max(1, ceil_div(k_len, bn(D)) // 4), 256))
 
 
 def test_python_binding_rejects_bad_dtype():

@@ -1,4 +1,4 @@
-"""The five workloads at full size on the GPU, checked against the oracle on sampled rows
+"""The workloads at full size on the GPU, checked against the oracle on sampled rows
 (config 1 in full). Inputs come from workloads.configs (seeded, synthetic)."""
 import numpy as np
 import pytest
@@ -75,4 +75,14 @@ def test_c5a_nan_padded():
 def test_c5b_decode():
     c = make_case("c5b")
     rows = np.array([[b, h, 0] for b in range(0, 32, 3) for h in range(8)], dtype=np.int32)
+    sampled_check(c, rows=rows)
+
+
+@pytest.mark.parametrize("name", ["n1a", "n1b", "n1c"])
+def test_n1_cached_prediction(name):
+    c = make_case(name)
+    say(f"  {name} splits {fa.num_splits(1, c.Sq, c.Sk, 8, 1, 64, 64, requested=0)}")
+    # every query row of every head: the rows are few, the keys many
+    rows = np.array([[0, h, i] for h in range(8) for i in range(0, c.Sq, max(1, c.Sq // 16))],
+                    dtype=np.int32)
     sampled_check(c, rows=rows)

@@ -113,6 +113,8 @@ def workload(name: str, dtype: Optional[str] = None) -> Spec:
     c4c  fp16 cross attention q[1,1000,6,64] k/v[1,1e6,6,64], split-KV heuristic
     c5a  bf16 D256 8:1 pack-GQA, q[4,1024,8,256], k/v[4,2048,1,256], seqused_k U[600,2048]
     c5b  bf16 D256 decode q[32,1,8,256], k/v[32,131072,1,256], causal, split-KV + combine
+    n1a/b/c  fp16 cached prediction: q[1,R,8,64] against k/v[1,300000,1,64] (MQA 8:1),
+             R = 16 / 64 / 256 query rows, non-causal, split-KV heuristic
     """
     s128 = f32(1.0 / math.sqrt(128.0))
     if name == "c1":
@@ -135,8 +137,15 @@ def workload(name: str, dtype: Optional[str] = None) -> Spec:
     if name == "c5b":
         return Spec(name, dtype or gen.BF16, 32, 1, 131072, 8, 1, 256, 256, True, f32(1 / 16), 52,
                     num_splits=0, pack_gqa=1)
+    if name in N1_ROWS:
+        return Spec(name, dtype or gen.FP16, 1, N1_ROWS[name], 300000, 8, 1, 64, 64, False, f32(1 / 8),
+                    N1_SEEDS[name], num_splits=0)
     raise KeyError(name)
 
 
-WORKLOADS = ("c1", "c2", "c3", "c4a", "c4b", "c4c", "c5a", "c5b")
+# short-query cached prediction: query rows per call and seeds
+N1_ROWS = {"n1a": 16, "n1b": 64, "n1c": 256}
+N1_SEEDS = {"n1a": 61, "n1b": 62, "n1c": 63}
+
+WORKLOADS = ("c1", "c2", "c3", "c4a", "c4b", "c4c", "c5a", "c5b", "n1a", "n1b", "n1c")
 
