@@ -106,7 +106,7 @@ struct Tile {
     static constexpr int VM_PER_TILE = 2 * LOADS;           // buffer loads a wave issues per tile
     static_assert(D == 16 || D == 64 || D == 128 || D == 256, "head dim");
     static_assert(LDS * WG_PER_CU <= 160 * 1024, "LDS budget");
-    static_assert(NB <= 4, "tile loop unrolled over at most four ring stages");
+    static_assert(NB <= 5, "tile loop unrolled over at most five ring stages");
     static_assert(GRANULES % NT == 0 || LOADS == 1, "a wave issues all of its loads of a tile or none");
     static_assert(GRANULES % 64 == 0, "whole waves per load instruction");
 };
@@ -218,6 +218,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     const int w_row = row0 + wave * T::NQB * 32;
     const int wi_lo = min(w_row, r_last) / gp;
     const int wi_hi = min(w_row + T::NQB * 32 - 1, r_last) / gp;
+    const bool wave_live = w_row < n_rows;
 
     int kv_end = k_len;
     if (CAUSAL) kv_end = min(k_len, i_hi + delta + 1);
@@ -566,16 +567,15 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     // waits until tile j+1 has landed (vmcnt counts this wave's buffer loads,
     // which complete in order) and the work-group meets at one barrier.
     auto wait_tiles_after_next = [&](int n_after) __attribute__((always_inline)) {
-        // s_waitcnt vmcnt(n_after * VM_PER_TILE); expcnt / lgkmcnt unconstrained
+        // s_waitcnt vmcnt(n_after * VM_PER_TILE), n_after <= PREFETCH - 1
         constexpr int L = T::VM_PER_TILE;
         static_assert((T::PREFETCH - 1) * L < 64, "vmcnt field");
-#define MI355_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
-        if (T::PREFETCH <= 1 || n_after <= 0) MI355_WAIT_VM(0);
-        else if (T::PREFETCH == 2 || n_after == 1) MI355_WAIT_VM(L);
-        else MI355_WAIT_VM(2 * L);
-#undef MI355_WAIT_VM
+        if (T::PREFETCH <= 1 || n_after <= 0) wait_vm_loads<0>();
+        else if (T::PREFETCH == 2 || n_after == 1) wait_vm_loads<L>();
+        else if (T::PREFETCH == 3 || n_after == 2) wait_vm_loads<2 * L>();
+        else wait_vm_loads<3 * L>();
     };
-    static_assert(T::PREFETCH >= 1 && T::PREFETCH <= 3, "wait_tiles_after_next covers up to two later tiles");
+    static_assert(T::PREFETCH >= 1 && T::PREFETCH <= 4, "wait_tiles_after_next covers up to three later tiles");
     auto issue = [&](int j, int st) __attribute__((always_inline)) {
         issue_tile(kbase, j, kstage(st), false);
         issue_tile(vbase, j, vstage(st), true);
@@ -587,19 +587,25 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         const int j0 = kb * T::BN;
         const bool need_mask = (j0 + T::BN > k_len) || (CAUSAL && (j0 + T::BN - 1 > wi_lo + delta));
         const bool band = BIAS && (wi_hi + delta - j0 >= 0) && (wi_lo + delta - (j0 + T::BN - 1) < p.E);
-        STile s;
-        qk(kstage(st), s);
-        // O is only touched in straight-line code (the rescale and PV), so the
-        // fast / slow branches merge no accumulator state
-        const bool fast = !need_mask && !band && p.c2 > 0.f;
-        if (fast) max_fast(s);
-        else max_slow(s, j0, band);
-        update_used_max();
-        rescale_acc();
-        if (fast) exp_fast(s);
-        else exp_slow(s, j0, band);
-        lo_decision();
-        pv(vstage(st), s);
+        // At D = 256 (decode, 8:1 pack-GQA) a wave with no rows in this tile, or
+        // whose rows see none of its keys (below the causal diagonal), only loads.
+        // (At smaller head dims the branch around the accumulators costs more
+        // than it saves.)
+        if (D != 256 || (wave_live && (!CAUSAL || j0 <= wi_hi + delta))) {
+            STile s;
+            qk(kstage(st), s);
+            // O is only touched in straight-line code (the rescale and PV), so the
+            // fast / slow branches merge no accumulator state
+            const bool fast = !need_mask && !band && p.c2 > 0.f;
+            if (fast) max_fast(s);
+            else max_slow(s, j0, band);
+            update_used_max();
+            rescale_acc();
+            if (fast) exp_fast(s);
+            else exp_slow(s, j0, band);
+            lo_decision();
+            pv(vstage(st), s);
+        }
         // tiles issued after kb+1: kb+2 .. min(kb+PREFETCH, kb_end-1)
         wait_tiles_after_next(min(kb + T::PREFETCH, kb_end - 1) - (kb + 1));
         __syncthreads();
@@ -609,12 +615,13 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         for (int j = kb_begin; j < first_end; j++) issue(j, j - kb_begin);
         wait_tiles_after_next(first_end - 1 - kb_begin);  // tile kb_begin has landed
         __syncthreads();
-        // unrolled over the ring stages (NB <= 4)
+        // unrolled over the ring stages (NB <= 5)
         for (int kb = kb_begin; kb < kb_end; kb += T::NB) {
             tile_step(kb, 0);
             if (T::NB > 1 && kb + 1 < kb_end) tile_step(kb + 1, 1 % T::NB);
             if (T::NB > 2 && kb + 2 < kb_end) tile_step(kb + 2, 2 % T::NB);
             if (T::NB > 3 && kb + 3 < kb_end) tile_step(kb + 3, 3 % T::NB);
+            if (T::NB > 4 && kb + 4 < kb_end) tile_step(kb + 4, 4 % T::NB);
         }
     }
 
