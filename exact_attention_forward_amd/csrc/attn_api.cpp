@@ -22,7 +22,9 @@ constexpr int kNumCUs = 256;  // MI355X compute units
 
 bool is_aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-bool head_dim_ok(int D) { return D == 16 || D == 64 || D == 128 || D == 256; }
+// head dims of q/k and of v: multiples of 8 from 8 to 256 (any pair; the kernel
+// runs the class of the larger one)
+bool head_dim_ok(int d) { return d >= 8 && d <= 256 && d % 8 == 0; }
 
 // product of non-negative ints, false if it reaches 2^62
 bool mul_ok(long long& acc, long long x) {
@@ -39,14 +41,19 @@ bool mul_ok(long long& acc, long long x) {
 struct Plan {
     bool varlen;
     int G, gp, n_hg, n_tiles, ns, nkb_max;
+    int dclass;  // head-dim class the kernel is compiled for
     long long rows_q;
     long long nblocks;
 };
 
 // Tile geometry shared with the kernels; returns false for sizes that cannot be planned.
-bool make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int is_varlen, int max_seqlen_q,
+bool make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_varlen, int max_seqlen_q,
                int max_seqlen_k, int pack_gqa, int num_splits, Plan& pl) {
-    if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || !head_dim_ok(D)) return false;
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || !head_dim_ok(D) ||
+        !head_dim_ok(Dv))
+        return false;
+    pl.dclass = head_dim_class(D > Dv ? D : Dv);
+    const int dc = pl.dclass;
     pl.varlen = is_varlen != 0;
     pl.G = Hq / Hkv;
     const bool pack = pack_gqa == 1 || (pack_gqa == -1 && pl.G > 1);
@@ -54,7 +61,7 @@ bool make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int is_varlen, int
     pl.n_hg = pack ? Hkv : Hq;
     const long long qmax = pl.varlen ? max_seqlen_q : Sq;
     const long long kmax = pl.varlen ? max_seqlen_k : Sk;
-    const int bm = tile_bm(D), bn = tile_bn(D);
+    const int bm = tile_bm(dc), bn = tile_bn(dc);
     const long long nt = (qmax * pl.gp + bm - 1) / bm;
     if (nt > INT32_MAX) return false;
     pl.n_tiles = (int)nt;
@@ -68,11 +75,11 @@ bool make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int is_varlen, int
         ns = num_splits;
         if (ns > pl.nkb_max) ns = pl.nkb_max;
         if (ns > ATTN_MAX_SPLITS) ns = ATTN_MAX_SPLITS;
-    } else if (base == 0 || base >= (long long)kNumCUs * tile_wg_per_cu(D)) {
+    } else if (base == 0 || base >= (long long)kNumCUs * tile_wg_per_cu(dc)) {
         ns = 1;
     } else {
         // one wave of resident work-groups: CUs x work-groups per CU
-        ns = (int)((long long)kNumCUs * tile_wg_per_cu(D) / base);
+        ns = (int)((long long)kNumCUs * tile_wg_per_cu(dc) / base);
         const int cap = pl.nkb_max / 4 > 0 ? pl.nkb_max / 4 : 1;
         if (ns > cap) ns = cap;
         if (ns > ATTN_MAX_SPLITS) ns = ATTN_MAX_SPLITS;
@@ -95,10 +102,10 @@ attn_status_t validate(const void* q, const void* k, const void* v, void* out, f
                        attn_dtype_t dtype, void* workspace, size_t workspace_bytes, Plan& pl) {
     if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_BAD_DTYPE;
     if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Dv <= 0) return ATTN_ERR_BAD_SHAPE;
-    if (D != Dv || !head_dim_ok(D)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+    if (!head_dim_ok(D) || !head_dim_ok(Dv)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
     if (Hq % Hkv) return ATTN_ERR_BAD_GQA;
     // a K/V tile (64 keys) must span fewer than 2^31 bytes: buffer offsets are 32-bit
-    if ((long long)Hkv * D > (1LL << 23)) return ATTN_ERR_BAD_SHAPE;
+    if ((long long)Hkv * (D > Dv ? D : Dv) > (1LL << 23)) return ATTN_ERR_BAD_SHAPE;
     if (!isfinite(scale)) return ATTN_ERR_BAD_SCALE;
     if (pack_gqa < -1 || pack_gqa > 1) return ATTN_ERR_BAD_ARG;
     if ((cu_q == nullptr) != (cu_k == nullptr)) return ATTN_ERR_BAD_VARLEN;
@@ -113,7 +120,10 @@ attn_status_t validate(const void* q, const void* k, const void* v, void* out, f
     long long nq = 1, nk = 1;
     if (!mul_ok(nq, varlen ? 1 : B) || !mul_ok(nq, Sq) || !mul_ok(nq, Hq) || !mul_ok(nq, D))
         return ATTN_ERR_BAD_SHAPE;
-    if (!mul_ok(nk, varlen ? 1 : B) || !mul_ok(nk, Sk) || !mul_ok(nk, Hkv) || !mul_ok(nk, D))
+    if (!mul_ok(nk, varlen ? 1 : B) || !mul_ok(nk, Sk) || !mul_ok(nk, Hkv) || !mul_ok(nk, D > Dv ? D : Dv))
+        return ATTN_ERR_BAD_SHAPE;
+    long long no = 1;
+    if (!mul_ok(no, varlen ? 1 : B) || !mul_ok(no, Sq) || !mul_ok(no, Hq) || !mul_ok(no, Dv))
         return ATTN_ERR_BAD_SHAPE;
     if (rel_bias) {
         if (rel_extent <= 0 || rel_extent % 128) return ATTN_ERR_BAD_REL_EXTENT;
@@ -123,7 +133,7 @@ attn_status_t validate(const void* q, const void* k, const void* v, void* out, f
     } else if (rel_extent != 0) {
         return ATTN_ERR_BAD_REL_EXTENT;
     }
-    if (!make_plan(B, Sq, Sk, Hq, Hkv, D, varlen, max_seqlen_q, max_seqlen_k, pack_gqa, num_splits, pl))
+    if (!make_plan(B, Sq, Sk, Hq, Hkv, D, Dv, varlen, max_seqlen_q, max_seqlen_k, pack_gqa, num_splits, pl))
         return ATTN_ERR_BAD_SHAPE;
     if (pl.nblocks > INT32_MAX) return ATTN_ERR_BAD_SHAPE;
     const bool has_rows = pl.rows_q > 0 && B > 0;
@@ -167,9 +177,8 @@ attn_status_t attn_check_args(const void* q, const void* k, const void* v, void*
 
 int attn_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_varlen,
                     int max_seqlen_q, int max_seqlen_k, int pack_gqa, int num_splits) {
-    if (D != Dv) return 0;
     Plan pl;
-    if (!make_plan(B, Sq, Sk, Hq, Hkv, D, is_varlen, max_seqlen_q, max_seqlen_k, pack_gqa, num_splits, pl))
+    if (!make_plan(B, Sq, Sk, Hq, Hkv, D, Dv, is_varlen, max_seqlen_q, max_seqlen_k, pack_gqa, num_splits, pl))
         return 0;
     return pl.ns;
 }
@@ -215,6 +224,8 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
     p.Sk = Sk;
     p.Hq = Hq;
     p.Hkv = Hkv;
+    p.D = D;
+    p.Dv = Dv;
     p.G = pl.G;
     p.gp = pl.gp;
     p.n_hg = pl.n_hg;
@@ -229,11 +240,11 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
     const bool split = pl.ns > 1;
     hipStream_t s = (hipStream_t)stream;
     if (log_enabled())
-        fprintf(stderr, "[attn] D=%d %s causal=%d varlen=%d bias=%d gp=%d n_hg=%d tiles=%d splits=%d grid=%lld\n",
-                D, bf ? "bf16" : "fp16", causal ? 1 : 0, pl.varlen ? 1 : 0, rel_bias ? 1 : 0, pl.gp, pl.n_hg,
+        fprintf(stderr, "[attn] D=%d Dv=%d class=%d %s causal=%d varlen=%d bias=%d gp=%d n_hg=%d tiles=%d splits=%d grid=%lld\n",
+                D, Dv, pl.dclass, bf ? "bf16" : "fp16", causal ? 1 : 0, pl.varlen ? 1 : 0, rel_bias ? 1 : 0, pl.gp, pl.n_hg,
                 pl.n_tiles, pl.ns, pl.nblocks);
     hipError_t e;
-    switch (D) {
+    switch (pl.dclass) {
         case 16: e = launch_fwd_d16(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, s); break;
         case 64: e = launch_fwd_d64(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, s); break;
         case 128: e = launch_fwd_d128(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, s); break;
@@ -252,6 +263,7 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
         c.Sq = Sq;
         c.ns = pl.ns;
         c.is_varlen = pl.varlen ? 1 : 0;
+        c.Dv = Dv;
         if (launch_combine(c, Dv, bf, s) != hipSuccess) return ATTN_ERR_HIP;
     }
     return ATTN_OK;
@@ -271,7 +283,7 @@ attn_status_t attn_combine(const float* o_partial, const float* lse_partial, int
     if (!o_partial || !lse_partial || !out) return ATTN_ERR_NULL_POINTER;
     if (!is_aligned(o_partial, 16) || !is_aligned(lse_partial, 4) || !is_aligned(out, 16) || !is_aligned(lse, 4))
         return ATTN_ERR_MISALIGNED;
-    if ((rows_q * Hq + 3) / 4 > INT32_MAX) return ATTN_ERR_BAD_SHAPE;
+    if (rows_q * Hq > INT32_MAX) return ATTN_ERR_BAD_SHAPE;  // one work-group per (row, head)
     CombineParams c;
     c.o_part = o_partial;
     c.lse_part = lse_partial;
@@ -282,6 +294,7 @@ attn_status_t attn_combine(const float* o_partial, const float* lse_partial, int
     c.Sq = Sq;
     c.ns = num_splits;
     c.is_varlen = is_varlen ? 1 : 0;
+    c.Dv = Dv;
     return launch_combine(c, Dv, dtype == ATTN_BF16, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -291,7 +304,7 @@ const char* attn_status_string(attn_status_t s) {
         case ATTN_ERR_NULL_POINTER: return "a required pointer is NULL";
         case ATTN_ERR_BAD_SHAPE: return "invalid or overflowing sizes";
         case ATTN_ERR_BAD_DTYPE: return "dtype must be bf16 or fp16";
-        case ATTN_ERR_UNSUPPORTED_HEAD_DIM: return "head dim must satisfy D == Dv in {16, 64, 128, 256}";
+        case ATTN_ERR_UNSUPPORTED_HEAD_DIM: return "head dims D and Dv must be multiples of 8 in [8, 256]";
         case ATTN_ERR_BAD_GQA: return "Hq must be a multiple of Hkv";
         case ATTN_ERR_BAD_REL_EXTENT: return "rel_extent must be a positive multiple of 128 and needs rel_bias";
         case ATTN_ERR_BAD_VARLEN: return "cu_seqlens_q/k must be given together with valid max_seqlen";

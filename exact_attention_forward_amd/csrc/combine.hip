@@ -80,13 +80,13 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const CombineParams p
     }
 
     const int dv0 = lane * PER;
-    const bool active = dv0 < DV;
+    const bool active = dv0 < p.Dv;  // Dv <= DV, a multiple of 8 (whole PER-column groups)
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; e++) acc[e] = 0.f;
     if (L != -INFINITY && active) {
-        const float* op = p.o_part + item * DV + dv0;
-        const long long ostride = lse_stride * DV;  // floats between splits
+        const float* op = p.o_part + item * p.Dv + dv0;
+        const long long ostride = lse_stride * p.Dv;  // floats between splits
         int s = wave;
         for (; s + 4 * (UNROLL - 1) < p.ns; s += 4 * UNROLL) {
             float w[UNROLL], x[UNROLL][PER];
@@ -117,7 +117,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const CombineParams p
         for (int e = 0; e < PER; e++) part[wave][dv0 + e] = acc[e];
     __syncthreads();
     if (wave == 0 && active) {
-        uint16_t* dst = p.out + item * DV + dv0;
+        uint16_t* dst = p.out + item * p.Dv + dv0;
 #pragma unroll
         for (int e = 0; e < PER; e++) {
             const int c = dv0 + e;
@@ -141,7 +141,7 @@ hipError_t launch_combine_t(const CombineParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_combine(const CombineParams& p, int Dv, bool bf16, hipStream_t s) {
-    switch (Dv) {
+    switch (head_dim_class(Dv)) {
         case 16: return bf16 ? launch_combine_t<16, true>(p, s) : launch_combine_t<16, false>(p, s);
         case 64: return bf16 ? launch_combine_t<64, true>(p, s) : launch_combine_t<64, false>(p, s);
         case 128: return bf16 ? launch_combine_t<128, true>(p, s) : launch_combine_t<128, false>(p, s);

@@ -246,11 +246,11 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     v8 qf[T::NQB][T::NC];
 #pragma unroll
     for (int qb = 0; qb < T::NQB; qb++) {
-        const uint16_t* qrow = p.q + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)D;
+        const uint16_t* qrow = p.q + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)p.D;
 #pragma unroll
         for (int c = 0; c < T::NC; c++) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (qvalid[qb]) x = *(const u32x4*)(qrow + 16 * c + 8 * hf);
+            u32x4 x = {0u, 0u, 0u, 0u};  // columns past D stay zero
+            if (qvalid[qb] && 16 * c + 8 * hf < p.D) x = *(const u32x4*)(qrow + 16 * c + 8 * hf);
             qf[qb][c] = __builtin_bit_cast(v8, x);
         }
     }
@@ -275,9 +275,10 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     // ---- K/V tiles: buffer loads straight into LDS (no register staging) ----
     // Rows past k_len lie outside the buffer range, so the hardware writes zeros
     // for them: padding (even NaN) never reaches the MFMAs.
-    const uint16_t* kbase = p.k + (k_off * p.Hkv + hk) * (long long)D;
-    const uint16_t* vbase = p.v + (k_off * p.Hkv + hk) * (long long)D;
-    const int row_bytes = p.Hkv * D * 2;  // bytes between consecutive keys
+    const uint16_t* kbase = p.k + (k_off * p.Hkv + hk) * (long long)p.D;
+    const uint16_t* vbase = p.v + (k_off * p.Hkv + hk) * (long long)p.Dv;
+    const int krow_bytes = p.Hkv * p.D * 2;   // bytes between consecutive keys of K
+    const int vrow_bytes = p.Hkv * p.Dv * 2;  // and of V
     auto kstage = [&](int st) __attribute__((always_inline)) { return smem + st * 2 * T::TILE_BYTES; };
     auto vstage = [&](int st) __attribute__((always_inline)) { return smem + st * 2 * T::TILE_BYTES + T::TILE_BYTES; };
 
@@ -285,8 +286,10 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         const int j0 = kb * T::BN;
         // every field of the descriptor is wave-uniform; saying so keeps the loads
         // free of the per-lane "waterfall" the compiler would otherwise wrap them in
+        const int row_bytes = is_v ? vrow_bytes : krow_bytes;
+        const int ng = (is_v ? p.Dv : p.D) >> 3;  // granules of a row that hold data
         const int nrec = __builtin_amdgcn_readfirstlane(max(0, min(T::BN, k_len - j0)) * row_bytes);
-        const uint64_t addr = (uint64_t)(base + (long long)j0 * p.Hkv * D);
+        const uint64_t addr = (uint64_t)((const char*)base + (long long)j0 * row_bytes);
         const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -304,8 +307,9 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
                     key = (g / (4 * T::NG)) * 4 + (g & 3);
                     c = (g >> 2) % T::NG;
                 }
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + g0 * 16), 16,
-                                                         key * row_bytes + c * 16, 0, 0, 0);
+                // columns past D (Dv): an offset past the range, so the load writes zeros
+                const int off = c < ng ? key * row_bytes + c * 16 : nrec;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + g0 * 16), 16, off, 0, 0, 0);
             }
         }
     };
@@ -638,13 +642,13 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         const long long lidx = VARLEN ? (long long)h * p.rows_q + q_off + i
                                       : ((long long)b * p.Hq + h) * p.Sq + i;
         if (!SPLIT) {
-            uint16_t* orow_p = p.out + orow * D;
+            uint16_t* orow_p = p.out + orow * p.Dv;
 #pragma unroll
             for (int dt = 0; dt < T::NDT; dt++)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; g4++) {
                     const int dv = 32 * dt + 8 * g4 + 4 * hf;
-                    if (dv < D) {
+                    if (dv < p.Dv) {
                         const unsigned lo = (unsigned)E::narrow(o[qb][dt][4 * g4 + 0] * inv) |
                                             ((unsigned)E::narrow(o[qb][dt][4 * g4 + 1] * inv) << 16);
                         const unsigned hi = (unsigned)E::narrow(o[qb][dt][4 * g4 + 2] * inv) |
@@ -654,13 +658,13 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
                 }
             if (p.lse && hf == 0) p.lse[lidx] = lse_v;
         } else {
-            float* op = p.o_part + ((long long)split * p.rows_q * p.Hq + orow) * D;
+            float* op = p.o_part + ((long long)split * p.rows_q * p.Hq + orow) * p.Dv;
 #pragma unroll
             for (int dt = 0; dt < T::NDT; dt++)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; g4++) {
                     const int dv = 32 * dt + 8 * g4 + 4 * hf;
-                    if (dv < D)
+                    if (dv < p.Dv)
                         *(f32x4*)(op + dv) = f32x4{o[qb][dt][4 * g4 + 0] * inv, o[qb][dt][4 * g4 + 1] * inv,
                                                    o[qb][dt][4 * g4 + 2] * inv, o[qb][dt][4 * g4 + 3] * inv};
                 }

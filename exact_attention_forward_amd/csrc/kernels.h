@@ -5,7 +5,14 @@
 
 namespace mi355attn {
 
-// Work-group geometry of the forward kernel for head dim D (D == Dv).
+// Head-dim class: the kernels are compiled for D, Dv up to 16, 64, 128 and 256;
+// a call with any D, Dv in 8..256 (multiples of 8) runs the smallest class that
+// holds both, with the K / V / Q columns past D (Dv) zero in registers and LDS.
+__host__ __device__ constexpr int head_dim_class(int d) {
+    return d <= 16 ? 16 : d <= 64 ? 64 : d <= 128 ? 128 : 256;
+}
+
+// Work-group geometry of the forward kernel for head-dim class D.
 //   4 waves of 64 lanes; each wave owns NQB blocks of 32 query rows
 //   (one MFMA 32x32 output column block per row block); BN keys per K/V tile.
 struct TileGeom {
@@ -36,6 +43,7 @@ struct FwdParams {
     const int* cu_k;
     const int* seqused_k;  // may be null
     int B, Sq, Sk, Hq, Hkv;
+    int D, Dv;             // head dims of q/k and of v / out (at most the class)
     int G;                 // Hq / Hkv
     int gp;                // query heads packed per tile row group (G with pack-GQA, else 1)
     int n_hg;              // head groups: Hkv when packed, else Hq
@@ -54,6 +62,7 @@ struct CombineParams {
     float* lse;            // may be null
     long long rows_q;      // rows of q's flattened order
     int Hq, Sq, ns, is_varlen;
+    int Dv;                // columns of a row (at most the class the kernel is compiled for)
 };
 
 hipError_t launch_fwd_d16(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,

@@ -49,7 +49,7 @@ typedef enum {
     ATTN_ERR_NULL_POINTER = 1,      /* a required pointer is NULL */
     ATTN_ERR_BAD_SHAPE = 2,         /* negative / zero / overflowing sizes */
     ATTN_ERR_BAD_DTYPE = 3,         /* dtype is not ATTN_BF16 or ATTN_FP16 */
-    ATTN_ERR_UNSUPPORTED_HEAD_DIM = 4, /* D != Dv, or D not in {16, 64, 128, 256} */
+    ATTN_ERR_UNSUPPORTED_HEAD_DIM = 4, /* D or Dv not a multiple of 8 in [8, 256] */
     ATTN_ERR_BAD_GQA = 5,           /* Hq is not a multiple of Hkv */
     ATTN_ERR_BAD_REL_EXTENT = 6,    /* rel_extent <= 0, not a multiple of 128, or given without rel_bias */
     ATTN_ERR_BAD_VARLEN = 7,        /* only one of cu_seqlens_q/k given, or bad max_seqlen */
@@ -104,8 +104,12 @@ typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1 } attn_dtype_t;
  *   the combine kernel runs on the same stream before the call returns.
  *   workspace may be NULL when no split is used.
  * Alignment: q, k, v, out and workspace 16 bytes; lse 4 bytes; rel_bias 2 bytes.
- * Limits: D = Dv in {16, 64, 128, 256}; Hkv * D <= 2^23; sizes must keep every element
- * count below 2^62.
+ * Head dims: D (q, k) and Dv (v, out) are each any multiple of 8 from 8 to 256
+ *   (head_dim and head_dim_v of the tml-fa4 "Argument contract"; 8..256 in steps
+ *   of 8 is the range the TabPFN issue thread gives for FA4 on sm_90);
+ *   D = Dv = 64, 128 and 256 run at full efficiency, other pairs on the kernel
+ *   of the next size up (16, 64, 128 or 256) with the extra columns zero.
+ * Limits: Hkv * max(D, Dv) <= 2^23; sizes must keep every element count below 2^62.
  */
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                        int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale,
@@ -159,7 +163,7 @@ size_t attn_fwd_workspace_size(int B, int Sq, int Hq, int Dv, int is_varlen, int
  *   (rounded to `dtype`); all splits empty -> out = 0, lse = -inf.
  * Layouts of out / lse as in attn_fwd (is_varlen picks dense or varlen LSE order;
  * dense needs Sq = per-batch length, varlen Sq = total_q). lse may be NULL.
- * 1 <= num_splits <= ATTN_MAX_SPLITS; Dv in {16, 64, 128, 256}.
+ * 1 <= num_splits <= ATTN_MAX_SPLITS; Dv a multiple of 8 in [8, 256].
  * Alignment: partials and out 16 bytes, lse 4 bytes.
  */
 attn_status_t attn_combine(const float* o_partial, const float* lse_partial, int num_splits,

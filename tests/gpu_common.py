@@ -152,10 +152,11 @@ class Case:
         return out[b, i, h], lse[b, h, i]
 
 
-def random_case(rng_seed, *, dtype, B, Sq, Sk, Hq, Hkv, D, causal=False, varlen_lens=None,
+def random_case(rng_seed, *, dtype, B, Sq, Sk, Hq, Hkv, D, Dv=None, causal=False, varlen_lens=None,
                 seqused=None, E=0, nan_pad=False, num_splits=1, pack_gqa=-1, name="case",
                 q_std=1.0):
-    """Seeded random inputs of the given shape (small test cases)."""
+    """Seeded random inputs of the given shape (small test cases); Dv defaults to D."""
+    Dv = Dv or D
     s = rng_seed
     cu_q = cu_k = max_q = max_k = None
     if varlen_lens is not None:
@@ -163,14 +164,14 @@ def random_case(rng_seed, *, dtype, B, Sq, Sk, Hq, Hkv, D, causal=False, varlen_
         cu_q, cu_k = gen.cu_seqlens(qls), gen.cu_seqlens(kls)
         Sq, Sk, B = int(cu_q[-1]), int(cu_k[-1]), len(qls)
         max_q, max_k = max(1, max(qls)), max(1, max(kls))
-        qshape, kshape = (Sq, Hq, D), (Sk, Hkv, D)
+        qshape, kshape, vshape = (Sq, Hq, D), (Sk, Hkv, D), (Sk, Hkv, Dv)
         rows_q = Sq
     else:
-        qshape, kshape = (B, Sq, Hq, D), (B, Sk, Hkv, D)
+        qshape, kshape, vshape = (B, Sq, Hq, D), (B, Sk, Hkv, D), (B, Sk, Hkv, Dv)
         rows_q = B * Sq
     q = gen.stream_normal_bits(s, 1, qshape, dtype, q_std)
     k = gen.stream_normal_bits(s, 2, kshape, dtype)
-    v = gen.stream_normal_bits(s, 3, kshape, dtype)
+    v = gen.stream_normal_bits(s, 3, vshape, dtype)
     bias = gen.stream_normal_bits(s, 4, (rows_q, Hq, E), dtype, 0.5) if E else None
     su = None if seqused is None else np.asarray(seqused, dtype=np.int32)
     if su is not None and nan_pad:
@@ -178,7 +179,7 @@ def random_case(rng_seed, *, dtype, B, Sq, Sk, Hq, Hkv, D, causal=False, varlen_
             if varlen_lens is None:
                 k[b, su[b]:] = NAN16[dtype]
                 v[b, su[b]:] = NAN16[dtype]
-    return Case(dtype=dtype, B=B, Sq=Sq, Sk=Sk, Hq=Hq, Hkv=Hkv, D=D, causal=causal, q=q, k=k,
+    return Case(dtype=dtype, B=B, Sq=Sq, Sk=Sk, Hq=Hq, Hkv=Hkv, D=D, Dv=Dv, causal=causal, q=q, k=k,
                 v=v, cu_q=cu_q, cu_k=cu_k, max_q=max_q, max_k=max_k, seqused=su, bias=bias,
                 num_splits=num_splits, pack_gqa=pack_gqa, name=name)
 

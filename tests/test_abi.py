@@ -64,8 +64,10 @@ def check(lib, **over):
 
 def test_valid_calls(lib):
     assert check(lib) == 0
-    for D in (16, 64, 128, 256):
+    for D in range(8, 257, 8):  # the head-dim family: multiples of 8 up to 256
         assert check(lib, D=D, Dv=D) == 0
+    for D, Dv in ((128, 64), (64, 128), (192, 128), (72, 72), (48, 48), (8, 256), (256, 8)):
+        assert check(lib, D=D, Dv=Dv) == 0
     assert check(lib, dtype=1) == 0
     assert check(lib, Hq=32, Hkv=8, causal=1) == 0
     assert check(lib, cu_q=A, cu_k=A, max_q=100, max_k=100, B=3, Sq=257, Sk=257) == 0
@@ -82,9 +84,12 @@ def test_valid_calls(lib):
     (dict(B=-1), "ATTN_ERR_BAD_SHAPE"),
     (dict(Sq=-3), "ATTN_ERR_BAD_SHAPE"),
     (dict(Hq=0), "ATTN_ERR_BAD_SHAPE"),
-    (dict(D=96, Dv=96), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
-    (dict(D=128, Dv=64), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(D=100, Dv=100), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(D=128, Dv=60), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(D=4, Dv=4), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(D=264, Dv=264), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
     (dict(D=512, Dv=512), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(D=0, Dv=64), "ATTN_ERR_BAD_SHAPE"),
     (dict(Hq=8, Hkv=3), "ATTN_ERR_BAD_GQA"),
     (dict(bias=A, E=100), "ATTN_ERR_BAD_REL_EXTENT"),
     (dict(bias=A, E=0), "ATTN_ERR_BAD_REL_EXTENT"),
@@ -135,6 +140,9 @@ def test_workspace_and_splits(lib):
     # never fewer than 4 key blocks per split
     assert lib.attn_num_splits(1, 1, 640, 1, 1, 64, 64, 0, 0, 0, -1, 0) == ceil_div(640, bn(64)) // 4
     assert lib.attn_num_splits(1, 1, 640, 1, 1, 256, 256, 0, 0, 0, -1, 0) == ceil_div(640, bn(256)) // 4
+    # a head-dim pair plans like the class of the larger dim
+    assert lib.attn_num_splits(1, 1, 640, 1, 1, 72, 72, 0, 0, 0, -1, 0) == ceil_div(640, bn(128)) // 4
+    assert lib.attn_num_splits(1, 1, 640, 1, 1, 128, 200, 0, 0, 0, -1, 0) == ceil_div(640, bn(256)) // 4
     # varlen sizes come from max_seqlen
     assert lib.attn_num_splits(4, 400, 400000, 8, 8, 128, 128, 1, 100, 100000, -1, 0) == \
         heuristic(4 * 8 * ceil_div(100, BM), 100000, 128)
@@ -144,7 +152,7 @@ BM = 128  # rows per work-group of the forward kernel
 
 
 def bn(D):
-    """Keys per key block of the forward kernel: 64 up to head dim 128, 32 at 256."""
+    """Keys per key block of the forward kernel: 64 up to head dim 128, 32 above."""
     return 64 if D <= 128 else 32
 
 
@@ -153,7 +161,7 @@ def ceil_div(a, b):
 
 
 def resident(D):
-    """Work-groups that fit on the chip at once: 256 CUs x 2 (D <= 128) or x 1 (D = 256)."""
+    """Work-groups that fit on the chip at once: 256 CUs x 2 (D <= 128) or x 1 (above)."""
     return 256 * (2 if D <= 128 else 1)
 
 
