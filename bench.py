@@ -17,9 +17,9 @@ Reported:
               workload, scaled to the same unit
   check       GPU vs oracle on those sampled rows
 
-Algorithmic work: 4*D FLOPs per visible (query row, key, head) triple (2*D for
-QK^T, 2*Dv for PV); masked, padded and skipped pairs count nothing. Decode
-bytes: every valid K and V element once, plus q, O and LSE.
+Algorithmic work: 2*D + 2*Dv FLOPs per visible (query row, key, head) triple (2*D for
+QK^T, 2*Dv for PV); masked, padded and skipped pairs count nothing. Decode bytes: every valid
+K and V element once, plus q, O and LSE.
 """
 from __future__ import annotations
 
