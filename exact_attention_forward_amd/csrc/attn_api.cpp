@@ -42,6 +42,7 @@ struct Plan {
     bool varlen;
     int G, gp, n_hg, n_tiles, ns, nkb_max;
     int dclass;  // head-dim class the kernel is compiled for
+    bool dsplit; // class 256 with at most 32 rows per tile: the waves share out the V columns
     long long rows_q;
     long long nblocks;
 };
@@ -65,6 +66,7 @@ bool make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_var
     const long long nt = (qmax * pl.gp + bm - 1) / bm;
     if (nt > INT32_MAX) return false;
     pl.n_tiles = (int)nt;
+    pl.dsplit = dc == 256 && qmax * pl.gp <= 32;
     pl.nkb_max = (int)((kmax + bn - 1) / bn);
     pl.rows_q = pl.varlen ? (long long)Sq : (long long)B * Sq;
     const long long base = (long long)B * pl.n_hg * pl.n_tiles;
@@ -240,15 +242,15 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
     const bool split = pl.ns > 1;
     hipStream_t s = (hipStream_t)stream;
     if (log_enabled())
-        fprintf(stderr, "[attn] D=%d Dv=%d class=%d %s causal=%d varlen=%d bias=%d gp=%d n_hg=%d tiles=%d splits=%d grid=%lld\n",
-                D, Dv, pl.dclass, bf ? "bf16" : "fp16", causal ? 1 : 0, pl.varlen ? 1 : 0, rel_bias ? 1 : 0, pl.gp, pl.n_hg,
+        fprintf(stderr, "[attn] D=%d Dv=%d class=%d dsplit=%d %s causal=%d varlen=%d bias=%d gp=%d n_hg=%d tiles=%d splits=%d grid=%lld\n",
+                D, Dv, pl.dclass, pl.dsplit ? 1 : 0, bf ? "bf16" : "fp16", causal ? 1 : 0, pl.varlen ? 1 : 0, rel_bias ? 1 : 0, pl.gp, pl.n_hg,
                 pl.n_tiles, pl.ns, pl.nblocks);
     hipError_t e;
     switch (pl.dclass) {
-        case 16: e = launch_fwd_d16(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, s); break;
-        case 64: e = launch_fwd_d64(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, s); break;
-        case 128: e = launch_fwd_d128(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, s); break;
-        case 256: e = launch_fwd_d256(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, s); break;
+        case 16: e = launch_fwd_d16(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, pl.dsplit, s); break;
+        case 64: e = launch_fwd_d64(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, pl.dsplit, s); break;
+        case 128: e = launch_fwd_d128(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, pl.dsplit, s); break;
+        case 256: e = launch_fwd_d256(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, pl.dsplit, s); break;
         default: return ATTN_ERR_UNSUPPORTED_COMBO;
     }
     if (e != hipSuccess) return ATTN_ERR_HIP;

@@ -1,11 +1,12 @@
-// Forward-kernel instances for head dim 256 (bf16/fp16 x causal x varlen x bias x split).
+// Forward-kernel instances for head-dim class 256 (bf16/fp16 x causal x varlen x bias x split
+// x dv split).
 #include "fwd_kernel.hpp"
 
 namespace mi355attn {
 
 hipError_t launch_fwd_d256(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
-                          bool split, hipStream_t s) {
-    return launch_fwd_any<256>(p, bf16, causal, varlen, bias, split, s);
+                          bool split, bool dsplit, hipStream_t s) {
+    return launch_fwd_any<256>(p, bf16, causal, varlen, bias, split, dsplit, s);
 }
 
 }  // namespace mi355attn

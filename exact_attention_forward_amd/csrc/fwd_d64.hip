@@ -4,8 +4,8 @@
 namespace mi355attn {
 
 hipError_t launch_fwd_d64(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
-                          bool split, hipStream_t s) {
-    return launch_fwd_any<64>(p, bf16, causal, varlen, bias, split, s);
+                          bool split, bool dsplit, hipStream_t s) {
+    return launch_fwd_any<64>(p, bf16, causal, varlen, bias, split, dsplit, s);
 }
 
 }  // namespace mi355attn

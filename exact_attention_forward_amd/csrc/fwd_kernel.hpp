@@ -150,9 +150,15 @@ __device__ __forceinline__ void wait_vm_loads() {
 __device__ __forceinline__ void wait_vm_all() { wait_vm_loads<0>(); }
 
 
-template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT>
+// DSPLIT (class 256, every tile at most 32 rows: decode): the four waves take the
+// same rows; each computes S and the softmax for all of them (identical values)
+// and accumulates a quarter of the V columns, so the PV MFMAs of a tile are shared
+// out instead of all falling to the one wave that holds rows.
+template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT, bool DSPLIT>
 __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const FwdParams p) {
     using T = Tile<D>;
+    static_assert(!DSPLIT || (D == 256 && T::NQB == 1), "dv split: class 256, one row block");
+    constexpr int ODT = DSPLIT ? T::NDT / 4 : T::NDT;  // dv blocks of O^T this wave accumulates
     using E = Elem<BF>;
     typedef typename E::v8 v8;
     typedef f32x16 STile[T::NQB][T::NKB];
@@ -215,7 +221,8 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     const int r_last = min(row0 + T::BM, n_rows) - 1;
     const int i_hi = r_last / gp;
     // query rows of this wave (a wave past the last row repeats the last one)
-    const int w_row = row0 + wave * T::NQB * 32;
+    const int w_row = row0 + (DSPLIT ? 0 : wave * T::NQB * 32);
+    const int dt0 = DSPLIT ? wave * ODT : 0;  // first dv block of this wave
     const int wi_lo = min(w_row, r_last) / gp;
     const int wi_hi = min(w_row + T::NQB * 32 - 1, r_last) / gp;
     const bool wave_live = w_row < n_rows;
@@ -235,7 +242,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     bool qvalid[T::NQB];
 #pragma unroll
     for (int qb = 0; qb < T::NQB; qb++) {
-        const int row = row0 + (wave * T::NQB + qb) * 32 + l32;
+        const int row = row0 + ((DSPLIT ? 0 : wave * T::NQB) + qb) * 32 + l32;
         qvalid[qb] = row < n_rows;
         const int rr = qvalid[qb] ? row : r_last;
         qi[qb] = rr / gp;
@@ -259,7 +266,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     // m_used is the max the exponentials and O are currently referred to. O and
     // l are only rescaled when m_run exceeds m_used by more than kTau, so
     // p = 2^(t - m_used) <= 2^kTau and the rescale is rare after the first tiles.
-    f32x16 o[T::NQB][T::NDT];
+    f32x16 o[T::NQB][ODT];
     float m_run[T::NQB], m_used[T::NQB], l_run[T::NQB];
 #pragma unroll
     for (int qb = 0; qb < T::NQB; qb++) {
@@ -267,7 +274,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         m_used[qb] = -INFINITY;
         l_run[qb] = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < T::NDT; dt++)
+        for (int dt = 0; dt < ODT; dt++)
 #pragma unroll
             for (int r = 0; r < 16; r++) o[qb][dt][r] = 0.f;
     }
@@ -375,7 +382,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
 #pragma unroll
             for (int qb = 0; qb < T::NQB; qb++)
 #pragma unroll
-                for (int dt = 0; dt < T::NDT; dt++) {
+                for (int dt = 0; dt < ODT; dt++) {
                     f32x16 x = o[qb][dt];
                     x *= alpha[qb];
                     if (T::WG_PER_CU == 1) asm volatile("" : "+a"(x));  // one block at a time
@@ -535,8 +542,8 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
 #pragma unroll
                 for (int e = 0; e < 8; e++) pt[qb][e] = E::to_elem(s[qb][t >> 1][8 * (t & 1) + e]);
 #pragma unroll
-            for (int dt = 0; dt < T::NDT; dt++) {
-                const v8 a = vfrag(vl, t, dt);
+            for (int dt = 0; dt < ODT; dt++) {
+                const v8 a = vfrag(vl, t, dt0 + dt);
 #pragma unroll
                 for (int qb = 0; qb < T::NQB; qb++) o[qb][dt] = E::mma(a, pt[qb], o[qb][dt]);
             }
@@ -555,8 +562,8 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
                         ptl[qb][e] = E::to_elem(need_lo[qb] ? pvv - (float)E::to_elem(pvv) : 0.f);
                     }
 #pragma unroll
-                for (int dt = 0; dt < T::NDT; dt++) {
-                    const v8 a = vfrag(vl, t, dt);
+                for (int dt = 0; dt < ODT; dt++) {
+                    const v8 a = vfrag(vl, t, dt0 + dt);
 #pragma unroll
                     for (int qb = 0; qb < T::NQB; qb++) o[qb][dt] = E::mma(a, ptl[qb], o[qb][dt]);
                 }
@@ -644,10 +651,10 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         if (!SPLIT) {
             uint16_t* orow_p = p.out + orow * p.Dv;
 #pragma unroll
-            for (int dt = 0; dt < T::NDT; dt++)
+            for (int dt = 0; dt < ODT; dt++)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; g4++) {
-                    const int dv = 32 * dt + 8 * g4 + 4 * hf;
+                    const int dv = 32 * (dt0 + dt) + 8 * g4 + 4 * hf;
                     if (dv < p.Dv) {
                         const unsigned lo = (unsigned)E::narrow(o[qb][dt][4 * g4 + 0] * inv) |
                                             ((unsigned)E::narrow(o[qb][dt][4 * g4 + 1] * inv) << 16);
@@ -656,27 +663,27 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
                         *(u32x2*)(orow_p + dv) = u32x2{lo, hi};
                     }
                 }
-            if (p.lse && hf == 0) p.lse[lidx] = lse_v;
+            if (p.lse && hf == 0 && (!DSPLIT || wave == 0)) p.lse[lidx] = lse_v;
         } else {
             float* op = p.o_part + ((long long)split * p.rows_q * p.Hq + orow) * p.Dv;
 #pragma unroll
-            for (int dt = 0; dt < T::NDT; dt++)
+            for (int dt = 0; dt < ODT; dt++)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; g4++) {
-                    const int dv = 32 * dt + 8 * g4 + 4 * hf;
+                    const int dv = 32 * (dt0 + dt) + 8 * g4 + 4 * hf;
                     if (dv < p.Dv)
                         *(f32x4*)(op + dv) = f32x4{o[qb][dt][4 * g4 + 0] * inv, o[qb][dt][4 * g4 + 1] * inv,
                                                    o[qb][dt][4 * g4 + 2] * inv, o[qb][dt][4 * g4 + 3] * inv};
                 }
-            if (hf == 0) p.lse_part[(long long)split * p.rows_q * p.Hq + lidx] = lse_v;
+            if (hf == 0 && (!DSPLIT || wave == 0)) p.lse_part[(long long)split * p.rows_q * p.Hq + lidx] = lse_v;
         }
     }
 }
 
 // ---- launch helpers ----
-template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT>
+template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT, bool DSPLIT>
 hipError_t launch_one(const FwdParams& p, hipStream_t s) {
-    const void* fn = (const void*)attn_fwd_kernel<D, BF, CAUSAL, VARLEN, BIAS, SPLIT>;
+    const void* fn = (const void*)attn_fwd_kernel<D, BF, CAUSAL, VARLEN, BIAS, SPLIT, DSPLIT>;
     constexpr unsigned lds = Tile<D>::LDS;
     static const hipError_t attr =
         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -688,9 +695,11 @@ hipError_t launch_one(const FwdParams& p, hipStream_t s) {
 
 typedef hipError_t (*FwdLauncher)(const FwdParams&, hipStream_t);
 
+// instance index bits: bf16, causal, varlen, bias, split, dv split
 template <int D, int I>
 hipError_t launch_idx(const FwdParams& p, hipStream_t s) {
-    return launch_one<D, (I & 1) != 0, (I & 2) != 0, (I & 4) != 0, (I & 8) != 0, (I & 16) != 0>(p, s);
+    return launch_one<D, (I & 1) != 0, (I & 2) != 0, (I & 4) != 0, (I & 8) != 0, (I & 16) != 0,
+                      (I & 32) != 0>(p, s);
 }
 
 template <int D, size_t... I>
@@ -698,11 +707,15 @@ constexpr std::array<FwdLauncher, sizeof...(I)> make_fwd_table(std::index_sequen
     return {&launch_idx<D, (int)I>...};
 }
 
+// dsplit is honoured at class 256 only (the host asks for it only there)
 template <int D>
 hipError_t launch_fwd_any(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias, bool split,
-                          hipStream_t s) {
-    static constexpr auto table = make_fwd_table<D>(std::make_index_sequence<32>{});
-    const int idx = (bf16 ? 1 : 0) | (causal ? 2 : 0) | (varlen ? 4 : 0) | (bias ? 8 : 0) | (split ? 16 : 0);
+                          bool dsplit, hipStream_t s) {
+    constexpr bool HAS_DSPLIT = D == 256;
+    static constexpr auto table = make_fwd_table<D>(std::make_index_sequence<HAS_DSPLIT ? 64 : 32>{});
+    if (dsplit && !HAS_DSPLIT) return hipErrorInvalidValue;
+    const int idx = (bf16 ? 1 : 0) | (causal ? 2 : 0) | (varlen ? 4 : 0) | (bias ? 8 : 0) | (split ? 16 : 0) |
+                    (dsplit ? 32 : 0);
     return table[idx](p, s);
 }
 

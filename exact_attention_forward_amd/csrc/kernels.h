@@ -66,13 +66,13 @@ struct CombineParams {
 };
 
 hipError_t launch_fwd_d16(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
-                          bool split, hipStream_t s);
+                          bool split, bool dsplit, hipStream_t s);
 hipError_t launch_fwd_d64(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
-                          bool split, hipStream_t s);
+                          bool split, bool dsplit, hipStream_t s);
 hipError_t launch_fwd_d128(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
-                           bool split, hipStream_t s);
+                           bool split, bool dsplit, hipStream_t s);
 hipError_t launch_fwd_d256(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
-                           bool split, hipStream_t s);
+                           bool split, bool dsplit, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int Dv, bool bf16, hipStream_t s);
 
 }  // namespace mi355attn

@@ -53,3 +53,14 @@ def test_rel_bias_band(D):
     c = random_case(7700 + D, dtype="bf16", B=2, Sq=0, Sk=0, Hq=4, Hkv=2, D=D, causal=True,
                     varlen_lens=(qls, kls), E=128, name=f"rel_bias D{D}")
     full_check(c)
+
+
+@pytest.mark.parametrize("D,Dv", [(256, 256), (200, 136), (136, 256), (256, 8)])
+@pytest.mark.parametrize("Sq,G", [(1, 8), (4, 8), (3, 2), (1, 1)])
+def test_decode_rows_share_waves(D, Dv, Sq, G):
+    """Class 256 with at most 32 rows per tile: every wave takes the same rows and a
+    quarter of the V columns. Causal, padded keys, several splits."""
+    c = random_case(7800 + D + Dv + 10 * Sq + G, dtype="bf16", B=3, Sq=Sq, Sk=2100, Hq=2 * G, Hkv=2,
+                    D=D, Dv=Dv, causal=True, seqused=[2100, 1333, 40], nan_pad=True, num_splits=0,
+                    name=f"decode D{D} Dv{Dv} Sq{Sq} G{G}")
+    full_check(c)
