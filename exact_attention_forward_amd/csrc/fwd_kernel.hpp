@@ -171,13 +171,29 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     const int hf = lane >> 5;
 
     // ---- work-group -> (batch, head group, split, row tile), XCD-aware ----
-    // Work-groups are handed to the 8 XCDs round-robin; give each XCD a
-    // contiguous range of logical ids so tiles that read the same K/V share an L2.
+    // Work-groups are handed to the 8 XCDs round-robin. The row tiles of one
+    // (batch, head group, split) read the same K/V and should share an L2.
+    // Dense: each XCD gets a contiguous eighth of the logical ids. Varlen: the
+    // work of a (batch, head group) follows its sequence length, so whole chunks
+    // of row tiles are dealt to the XCDs in turn (chunk c to XCD c % 8), which
+    // spreads unequal sequences over all eight; the last, incomplete round of
+    // eight chunks stays round-robin.
     int lid;
     {
         const int nb = p.nblocks, bid = blockIdx.x;
-        const int q8 = nb >> 3, r8 = nb & 7, x = bid & 7, slot = bid >> 3;
-        lid = (x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8) + slot;
+        if (!VARLEN) {
+            const int q8 = nb >> 3, r8 = nb & 7, x = bid & 7, slot = bid >> 3;
+            lid = (x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8) + slot;
+        } else {
+            const int C = p.n_tiles;
+            const long long full = (long long)(nb / (8LL * C)) * 8 * C;
+            if (bid < full) {
+                const int x = bid & 7, slot = bid >> 3;
+                lid = ((slot / C) * 8 + x) * C + slot % C;
+            } else {
+                lid = bid;
+            }
+        }
     }
     int tile = lid % p.n_tiles;
     int rest = lid / p.n_tiles;
