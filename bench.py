@@ -275,6 +275,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="keep warming up (untimed steps) until this much time has passed as well: "
+                         "the GPU needs some hundred milliseconds of load to reach its steady clocks, "
+                         "longer than a few steps of a sub-millisecond call")
     ap.add_argument("--workload", default="c2", choices=sorted(DESCRIPTION))
     ap.add_argument("--dtype", default=None, choices=["bf16", "fp16"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -349,9 +353,15 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x elementwise copy of 1 GiB")
 
-    for _ in range(args.warmup):
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
         fa.attn_fwd(q, k, v, **kw)
+        n_warm += 1
+        if n_warm % 16 == 0:
+            torch.cuda.synchronize()  # keep the host from running ahead of the clock
     torch.cuda.synchronize()
+    log(f"warm-up: {n_warm} untimed steps in {time.perf_counter() - t_w:.2f} s")
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -390,7 +400,7 @@ def main():
 
     result = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "warmup": args.warmup, "warmup_steps_run": n_warm, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic",
         "config": {"workload": f"{args.workload}: {DESCRIPTION[args.workload]}", "B": spec.B,
                    "Sq": spec.Sq, "Sk": spec.Sk, "Hq": spec.Hq, "Hkv": spec.Hkv, "D": spec.D,

@@ -444,54 +444,74 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     // Tiles that cross the key bound, the causal diagonal or the bias band (or scale <= 0).
     // Per element the arithmetic is the fast path's (one FMA into exp2, with the
     // bias term folded into the addend), so the result of a row does not depend on
-    // which path a tile takes; masked keys get p = 0. The mask and the bias term
-    // are evaluated again in phase 2 (the bias row is then in cache) rather than
-    // kept in registers across the rescale.
-    auto slow_term = [&](int qb, int kb2, int r, int j0, bool band, const uint16_t* brow)
+    // which path a tile takes; masked keys get p = 0. The mask is evaluated again
+    // in phase 2 rather than kept in registers across the rescale.
+    // The bias of a band tile is read once, at the start of the tile step and
+    // before that step's K/V prefetch goes out (waiting for these loads then does
+    // not wait for the prefetch), into 16-bit pairs; elements outside the band or
+    // not visible hold 0.
+    typedef uint32_t BiasBits[T::NQB][T::NKB][8];
+    auto bias_row = [&](int qb) __attribute__((always_inline)) {
+        return BIAS ? p.bias + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)p.E : nullptr;
+    };
+    auto load_bias = [&](BiasBits& bb, int j0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) {
+            const uint16_t* brow = bias_row(qb);
+            const int i = qi[qb];
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++)
+#pragma unroll
+                for (int r2 = 0; r2 < 8; r2++) {
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int e = 0; e < 2; e++) {
+                        const int j = j0 + kb2 * 32 + acc_row(2 * r2 + e, hf);
+                        const int d = i + delta - j;
+                        const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
+                        if (vis && qvalid[qb] && d >= 0 && d < p.E) w |= (uint32_t)brow[d] << (16 * e);
+                    }
+                    bb[qb][kb2][r2] = w;
+                }
+        }
+    };
+    auto slow_term = [&](int qb, int kb2, int r, int j0, bool band, const BiasBits& bb)
         __attribute__((always_inline)) {
         const int i = qi[qb];
         const int j = j0 + kb2 * 32 + acc_row(r, hf);
         const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
         float b2 = 0.f;
-        if (BIAS && band) {
-            const int d = i + delta - j;
-            if (vis && qvalid[qb] && d >= 0 && d < p.E) b2 = E::widen(brow[d]) * kLog2e;
-        }
+        if (BIAS && band) b2 = E::widen((uint16_t)(bb[qb][kb2][r >> 1] >> (16 * (r & 1)))) * kLog2e;
         return vis ? b2 : -INFINITY;  // -inf marks a masked key
     };
-    auto bias_row = [&](int qb) __attribute__((always_inline)) {
-        return BIAS ? p.bias + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)p.E : nullptr;
-    };
-    auto max_slow = [&](STile& s, int j0, bool band) __attribute__((always_inline)) {
+    auto max_slow = [&](STile& s, int j0, bool band, const BiasBits& bb) __attribute__((always_inline)) {
         // opaque copy: keeps the per-element key indices inside the slow path
         // instead of letting them be hoisted onto the fast path
         asm volatile("" : "+s"(j0));
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
             float mx = -INFINITY;
-            const uint16_t* brow = bias_row(qb);
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const float b2 = slow_term(qb, kb2, r, j0, band, brow);
+                    const float b2 = slow_term(qb, kb2, r, j0, band, bb);
                     mx = fmaxf(mx, b2 == -INFINITY ? -INFINITY : __builtin_fmaf(s[qb][kb2][r], p.c2, b2));
                 }
             m_run[qb] = fmaxf(m_run[qb], partner_max(mx));
         }
     };
-    auto exp_slow = [&](STile& s, int j0, bool band) __attribute__((always_inline)) {
+    auto exp_slow = [&](STile& s, int j0, bool band, const BiasBits& bb) __attribute__((always_inline)) {
         asm volatile("" : "+s"(j0));
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
             const float mu = m_used[qb] == -INFINITY ? 0.f : m_used[qb];
-            const uint16_t* brow = bias_row(qb);
             float rs = 0.f;
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const float b2 = slow_term(qb, kb2, r, j0, band, brow);
+                    const float b2 = slow_term(qb, kb2, r, j0, band, bb);
                     const float pv = b2 == -INFINITY ? 0.f
                                                      : __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, b2 - mu));
                     s[qb][kb2][r] = pv;
@@ -610,10 +630,12 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     // one key tile; st = (kb - kb_begin) % NB is a literal at every call site, so all
     // LDS addresses are a per-lane base plus an immediate offset
     auto tile_step = [&](int kb, int st) __attribute__((always_inline)) {
-        if (kb + T::PREFETCH < kb_end) issue(kb + T::PREFETCH, (st + T::PREFETCH) % T::NB);
         const int j0 = kb * T::BN;
         const bool need_mask = (j0 + T::BN > k_len) || (CAUSAL && (j0 + T::BN - 1 > wi_lo + delta));
         const bool band = BIAS && (wi_hi + delta - j0 >= 0) && (wi_lo + delta - (j0 + T::BN - 1) < p.E);
+        BiasBits bb;
+        if (BIAS && band) load_bias(bb, j0);
+        if (kb + T::PREFETCH < kb_end) issue(kb + T::PREFETCH, (st + T::PREFETCH) % T::NB);
         // At D = 256 (decode, 8:1 pack-GQA) a wave with no rows in this tile, or
         // whose rows see none of its keys (below the causal diagonal), only loads.
         // (At smaller head dims the branch around the accumulators costs more
@@ -625,11 +647,11 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
             // fast / slow branches merge no accumulator state
             const bool fast = !need_mask && !band && p.c2 > 0.f;
             if (fast) max_fast(s);
-            else max_slow(s, j0, band);
+            else max_slow(s, j0, band, bb);
             update_used_max();
             rescale_acc();
             if (fast) exp_fast(s);
-            else exp_slow(s, j0, band);
+            else exp_slow(s, j0, band, bb);
             lo_decision();
             pv(vstage(st), s);
         }
