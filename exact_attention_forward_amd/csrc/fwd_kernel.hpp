@@ -630,12 +630,15 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     // one key tile; st = (kb - kb_begin) % NB is a literal at every call site, so all
     // LDS addresses are a per-lane base plus an immediate offset
     auto tile_step = [&](int kb, int st) __attribute__((always_inline)) {
+        if (!BIAS && kb + T::PREFETCH < kb_end) issue(kb + T::PREFETCH, (st + T::PREFETCH) % T::NB);
         const int j0 = kb * T::BN;
         const bool need_mask = (j0 + T::BN > k_len) || (CAUSAL && (j0 + T::BN - 1 > wi_lo + delta));
         const bool band = BIAS && (wi_hi + delta - j0 >= 0) && (wi_lo + delta - (j0 + T::BN - 1) < p.E);
         BiasBits bb;
-        if (BIAS && band) load_bias(bb, j0);
-        if (kb + T::PREFETCH < kb_end) issue(kb + T::PREFETCH, (st + T::PREFETCH) % T::NB);
+        if (BIAS) {
+            if (band) load_bias(bb, j0);
+            if (kb + T::PREFETCH < kb_end) issue(kb + T::PREFETCH, (st + T::PREFETCH) % T::NB);
+        }
         // At D = 256 (decode, 8:1 pack-GQA) a wave with no rows in this tile, or
         // whose rows see none of its keys (below the causal diagonal), only loads.
         // (At smaller head dims the branch around the accumulators costs more
