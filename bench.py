@@ -45,6 +45,7 @@ DESCRIPTION = {
     "c1": "non-causal MHA [1,257,8,128]",
     "c2": "non-causal MHA [1,20480,56,128] (video joint attention)",
     "c3": "varlen causal GQA 32/8 D128 + rel_bias E256, 8 seqs len U[512,8192]",
+    "c3r": "c3 with the bias produced in the kernel from r [T,32,16] . rel_proj [16,256]",
     "c4a": "self-attention [256,10000,6,64]",
     "c4b": "feature attention [100,100000,4,16]",
     "c4c": "cross attention q[1,1000,6,64] k/v[1,1e6,6,64], split-KV heuristic",
@@ -228,6 +229,8 @@ def cpu_baseline(spec, x, out, lse, target_s, threads):
               D=spec.D, Dv=spec.Dv, scale=spec.scale, causal=spec.causal,
               cu_seqlens_q=x.get("cu_seqlens_q"), cu_seqlens_k=x.get("cu_seqlens_k"),
               seqused_k=x.get("seqused_k"), rel_bias=x.get("rel_bias"), threads=threads)
+    if "rel_r" in x:  # fused producer: the oracle gets the bias r . rel_proj makes
+        kw["rel_bias"] = oracle_mod.rel_bias_from_proj(x["rel_r"], x["rel_proj"], spec.dtype)
     cu = x.get("cu_seqlens_q")
 
     def row_flops(rows):
@@ -332,6 +335,9 @@ def main():
         kw["seqused_k"] = torch.from_numpy(x["seqused_k"]).cuda()
     if "rel_bias" in x:
         kw["rel_bias"] = dev16(x["rel_bias"])
+    if "rel_r" in x:
+        kw["rel_r"] = dev16(x["rel_r"])
+        kw["rel_proj"] = dev16(x["rel_proj"])
     # preallocate everything: the timed calls allocate nothing
     out, lse = fa.attn_fwd(q, k, v, **kw)
     ns = fa.num_splits(spec.B, spec.Sq, spec.Sk, spec.Hq, spec.Hkv, spec.D, spec.Dv,

@@ -40,6 +40,8 @@ _Z = ctypes.c_size_t
 SIGNATURES = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _I, _P,
                       _P, _I, _I, _I, _I, _P, _Z, _P]),
+    "attn_fwd_rel_proj": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _I,
+                               _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]),
     "attn_check_args": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _I,
                              _P, _P, _I, _I, _I, _I, _P, _Z]),
     "attn_num_splits": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
@@ -126,11 +128,13 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
              cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: Optional[int] = None,
              max_seqlen_k: Optional[int] = None, seqused_k=None, rel_bias=None,
              num_splits: int = 1, pack_gqa: int = -1, out=None, lse=None,
-             return_lse: bool = True, workspace=None, stream=None):
+             return_lse: bool = True, workspace=None, stream=None, rel_r=None, rel_proj=None):
     """Fused attention forward. Returns (out, lse); lse is None if return_lse is False.
 
     Dense: q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D]; lse [B, Hq, Sq].
     Varlen: q [total_q, Hq, D], k/v [total_k, Hkv, D], cu_seqlens int32 [B+1]; lse [Hq, total_q].
+    rel_r [rows_q, Hq, d_rel] with rel_proj [d_rel, E] (instead of rel_bias): the bias is their
+    product, formed inside the kernel (attn_fwd_rel_proj).
     out / lse / workspace are allocated with torch when not given (the allocation-free
     form passes all three, as forward_static does).
     """
@@ -170,7 +174,15 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
         out = torch.empty(out_shape, dtype=q.dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    if rel_r is not None or rel_proj is not None:
+        if rel_bias is not None or rel_r is None or rel_proj is None:
+            raise ValueError("pass rel_r with rel_proj, or rel_bias, not both")
+        for name, t in (("rel_r", rel_r), ("rel_proj", rel_proj)):
+            if not t.is_contiguous() or t.dtype != q.dtype:
+                raise ValueError(f"{name} must be contiguous and of q's dtype")
     E = 0 if rel_bias is None else int(rel_bias.shape[-1])
+    if rel_proj is not None:
+        E = int(rel_proj.shape[1])
     ns = lib.attn_num_splits(B, Sq, Sk, Hq, Hkv, D, Dv, int(varlen), max_seqlen_q, max_seqlen_k,
                              pack_gqa, num_splits)
     ws_bytes = 0
@@ -180,10 +192,18 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
         else:
             ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, Dv,
-                      float(scale), int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-                      max_seqlen_q, max_seqlen_k, _ptr(seqused_k), _ptr(rel_bias), E, num_splits,
-                      pack_gqa, dtype, _ptr(workspace), ws_bytes, _stream_handle(stream, q.device))
+    if rel_r is not None:
+        st = lib.attn_fwd_rel_proj(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D,
+                                   Dv, float(scale), int(bool(causal)), _ptr(cu_seqlens_q),
+                                   _ptr(cu_seqlens_k), max_seqlen_q, max_seqlen_k, _ptr(seqused_k),
+                                   _ptr(rel_r), _ptr(rel_proj), int(rel_proj.shape[0]), E, num_splits,
+                                   pack_gqa, dtype, _ptr(workspace), ws_bytes,
+                                   _stream_handle(stream, q.device))
+    else:
+        st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, Dv,
+                          float(scale), int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                          max_seqlen_q, max_seqlen_k, _ptr(seqused_k), _ptr(rel_bias), E, num_splits,
+                          pack_gqa, dtype, _ptr(workspace), ws_bytes, _stream_handle(stream, q.device))
     _check(st)
     return out, (lse if return_lse else None)
 

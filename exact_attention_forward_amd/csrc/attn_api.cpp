@@ -191,6 +191,33 @@ size_t attn_fwd_workspace_size(int B, int Sq, int Hq, int Dv, int is_varlen, int
     return workspace_bytes_for(rows_q, Hq, Dv, num_splits);
 }
 
+namespace {
+
+// LDS the fused producer needs for the bias rows of one work-group: BM rows x E values
+long long rel_rows_lds_bytes(int dclass, int rel_extent) {
+    return (long long)tile_bm(dclass) * rel_extent * 2;
+}
+
+// The fused-producer arguments on top of validate(): r and rel_proj given, d_rel a
+// multiple of 8 in [8, 256], r 16-byte aligned, and the bias rows fitting in LDS.
+attn_status_t validate_rel_proj(const void* rel_r, const void* rel_proj, int d_rel, int rel_extent,
+                                const Plan& pl) {
+    if (!rel_r || !rel_proj) return ATTN_ERR_NULL_POINTER;
+    if (d_rel < 8 || d_rel > 256 || d_rel % 8) return ATTN_ERR_BAD_ARG;
+    if (!is_aligned(rel_r, 16) || !is_aligned(rel_proj, 2)) return ATTN_ERR_MISALIGNED;
+    if (tile_ring_bytes(pl.dclass) + rel_rows_lds_bytes(pl.dclass, rel_extent) > kLdsBytesPerCU)
+        return ATTN_ERR_UNSUPPORTED_COMBO;
+    return ATTN_OK;
+}
+
+attn_status_t run_fwd(const Plan& pl, const void* q, const void* k, const void* v, void* out, float* lse,
+                      int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale, int causal,
+                      const int* cu_seqlens_q, const int* cu_seqlens_k, const int* seqused_k,
+                      const void* rel_bias, const void* rel_r, const void* rel_proj, int d_rel,
+                      int rel_extent, attn_dtype_t dtype, void* workspace, void* stream);
+
+}  // namespace
+
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                        int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale, int causal,
                        const int* cu_seqlens_q, const int* cu_seqlens_k, int max_seqlen_q,
@@ -204,6 +231,42 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
                  workspace, workspace_bytes, pl);
     if (st != ATTN_OK) return st;
     if (pl.nblocks == 0) return ATTN_OK;  // no rows to compute
+    return run_fwd(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, Dv, scale, causal, cu_seqlens_q,
+                   cu_seqlens_k, seqused_k, rel_bias, nullptr, nullptr, 0, rel_extent, dtype, workspace,
+                   stream);
+}
+
+attn_status_t attn_fwd_rel_proj(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                                int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale, int causal,
+                                const int* cu_seqlens_q, const int* cu_seqlens_k, int max_seqlen_q,
+                                int max_seqlen_k, const int* seqused_k, const void* rel_r,
+                                const void* rel_proj, int d_rel, int rel_extent, int num_splits,
+                                int pack_gqa, attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    Plan pl;
+    // validate as a call with a bias tensor (r stands in for its pointer: same row
+    // order and dtype), then the producer's own arguments
+    attn_status_t st =
+        validate(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, Dv, scale, cu_seqlens_q, cu_seqlens_k,
+                 max_seqlen_q, max_seqlen_k, rel_r ? rel_r : rel_proj, rel_extent, num_splits, pack_gqa,
+                 dtype, workspace, workspace_bytes, pl);
+    if (st != ATTN_OK) return st;
+    st = validate_rel_proj(rel_r, rel_proj, d_rel, rel_extent, pl);
+    if (st != ATTN_OK) return st;
+    if (pl.nblocks == 0) return ATTN_OK;
+    return run_fwd(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, Dv, scale, causal, cu_seqlens_q,
+                   cu_seqlens_k, seqused_k, nullptr, rel_r, rel_proj, d_rel, rel_extent, dtype, workspace,
+                   stream);
+}
+
+namespace {
+
+attn_status_t run_fwd(const Plan& pl, const void* q, const void* k, const void* v, void* out, float* lse,
+                      int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale, int causal,
+                      const int* cu_seqlens_q, const int* cu_seqlens_k, const int* seqused_k,
+                      const void* rel_bias, const void* rel_r, const void* rel_proj, int d_rel,
+                      int rel_extent, attn_dtype_t dtype, void* workspace, void* stream) {
+    const bool with_bias = rel_bias != nullptr || rel_r != nullptr;
 
     FwdParams p;
     p.q = (const uint16_t*)q;
@@ -212,6 +275,10 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
     p.out = (uint16_t*)out;
     p.lse = lse;
     p.bias = (const uint16_t*)rel_bias;
+    p.rel_r = (const uint16_t*)rel_r;
+    p.rel_proj = (const uint16_t*)rel_proj;
+    p.d_rel = d_rel;
+    p.lds_extra = rel_r ? (int)rel_rows_lds_bytes(pl.dclass, rel_extent) : 0;
     p.o_part = nullptr;
     p.lse_part = nullptr;
     if (pl.ns > 1) {
@@ -233,7 +300,7 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
     p.n_hg = pl.n_hg;
     p.n_tiles = pl.n_tiles;
     p.ns = pl.ns;
-    p.E = rel_bias ? rel_extent : 0;
+    p.E = with_bias ? rel_extent : 0;
     p.nblocks = (int)pl.nblocks;
     p.c2 = scale * 1.4426950408889634f;
     p.rows_q = pl.rows_q;
@@ -243,14 +310,14 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
     hipStream_t s = (hipStream_t)stream;
     if (log_enabled())
         fprintf(stderr, "[attn] D=%d Dv=%d class=%d dsplit=%d %s causal=%d varlen=%d bias=%d gp=%d n_hg=%d tiles=%d splits=%d grid=%lld\n",
-                D, Dv, pl.dclass, pl.dsplit ? 1 : 0, bf ? "bf16" : "fp16", causal ? 1 : 0, pl.varlen ? 1 : 0, rel_bias ? 1 : 0, pl.gp, pl.n_hg,
+                D, Dv, pl.dclass, pl.dsplit ? 1 : 0, bf ? "bf16" : "fp16", causal ? 1 : 0, pl.varlen ? 1 : 0, with_bias ? 1 : 0, pl.gp, pl.n_hg,
                 pl.n_tiles, pl.ns, pl.nblocks);
     hipError_t e;
     switch (pl.dclass) {
-        case 16: e = launch_fwd_d16(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, pl.dsplit, s); break;
-        case 64: e = launch_fwd_d64(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, pl.dsplit, s); break;
-        case 128: e = launch_fwd_d128(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, pl.dsplit, s); break;
-        case 256: e = launch_fwd_d256(p, bf, causal != 0, pl.varlen, rel_bias != nullptr, split, pl.dsplit, s); break;
+        case 16: e = launch_fwd_d16(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s); break;
+        case 64: e = launch_fwd_d64(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s); break;
+        case 128: e = launch_fwd_d128(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s); break;
+        case 256: e = launch_fwd_d256(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s); break;
         default: return ATTN_ERR_UNSUPPORTED_COMBO;
     }
     if (e != hipSuccess) return ATTN_ERR_HIP;
@@ -270,6 +337,8 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
     }
     return ATTN_OK;
 }
+
+}  // namespace
 
 attn_status_t attn_combine(const float* o_partial, const float* lse_partial, int num_splits, void* out,
                            float* lse, int B, int Sq, int Hq, int Dv, int is_varlen, attn_dtype_t dtype,

@@ -101,6 +101,7 @@ struct Tile {
     static constexpr int NB = PREFETCH + 1;       // LDS ring stages, each a K tile and a V tile
     static constexpr int WG_PER_CU = tile_wg_per_cu(D);
     static constexpr int LDS = NB * 2 * TILE_BYTES;
+    static_assert(LDS == tile_ring_bytes(D), "host and kernel agree on the ring size");
     static constexpr int GRANULES = BN * NG;      // 16-byte granules per tile
     static constexpr int LOADS = (GRANULES + NT - 1) / NT;  // per thread, per K (or V) tile
     static constexpr int VM_PER_TILE = 2 * LOADS;           // buffer loads a wave issues per tile
@@ -454,10 +455,14 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     auto bias_row = [&](int qb) __attribute__((always_inline)) {
         return BIAS ? p.bias + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)p.E : nullptr;
     };
+    // fused producer: the bias rows of the work-group, [BM][E], built in LDS
+    const bool fused_bias = BIAS && p.rel_r != nullptr;
+    uint16_t* bias_lds = (uint16_t*)(smem + T::LDS);
     auto load_bias = [&](BiasBits& bb, int j0) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
-            const uint16_t* brow = bias_row(qb);
+            const uint16_t* brow = fused_bias ? bias_lds + ((wave * T::NQB + qb) * 32 + l32) * p.E
+                                              : bias_row(qb);
             const int i = qi[qb];
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
@@ -663,6 +668,35 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         __syncthreads();
     };
     if (kb_begin < kb_end) {
+        if (fused_bias) {
+            // tml-fa4 page: rel_bias = r . rel_proj (the einsum over d_rel). Each wave builds
+            // the rows of its queries: C[32 rows x 32 d] = R[32 x d_rel] . rel_proj[d_rel x 32]
+            // on the MFMA (A = the lane's r row, B = a rel_proj column block), rounded to
+            // the input dtype as a materialised rel_bias would be, into LDS.
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++) {
+                const uint16_t* rrow = p.rel_r + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)p.d_rel;
+                uint16_t* out_rows = bias_lds + (wave * T::NQB + qb) * 32 * p.E;
+                for (int db = 0; db < p.E / 32; db++) {
+                    f32x16 c = {};
+                    for (int k0 = 0; k0 < p.d_rel; k0 += 16) {
+                        const int ka = k0 + 8 * hf;  // this lane's 8 contraction indices
+                        u32x4 a = {0u, 0u, 0u, 0u};
+                        if (qvalid[qb] && ka < p.d_rel) a = *(const u32x4*)(rrow + ka);
+                        u32x4 bw = {0u, 0u, 0u, 0u};
+                        if (ka < p.d_rel) {
+                            const uint16_t* pc = p.rel_proj + (long long)ka * p.E + 32 * db + l32;
+#pragma unroll
+                            for (int e = 0; e < 8; e += 2)
+                                bw[e >> 1] = (uint32_t)pc[e * p.E] | ((uint32_t)pc[(e + 1) * p.E] << 16);
+                        }
+                        c = E::mma(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, bw), c);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; r++) out_rows[acc_row(r, hf) * p.E + 32 * db + l32] = E::narrow(c[r]);
+                }
+            }
+        }
         const int first_end = min(kb_begin + T::PREFETCH, kb_end);
         for (int j = kb_begin; j < first_end; j++) issue(j, j - kb_begin);
         wait_tiles_after_next(first_end - 1 - kb_begin);  // tile kb_begin has landed
@@ -725,10 +759,13 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
 template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT, bool DSPLIT>
 hipError_t launch_one(const FwdParams& p, hipStream_t s) {
     const void* fn = (const void*)attn_fwd_kernel<D, BF, CAUSAL, VARLEN, BIAS, SPLIT, DSPLIT>;
-    constexpr unsigned lds = Tile<D>::LDS;
+    // bias instances may carry the fused producer's rows past the ring
+    constexpr unsigned lds_max = BIAS ? kLdsBytesPerCU : Tile<D>::LDS;
     static const hipError_t attr =
-        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
     if (attr != hipSuccess) return attr;
+    const unsigned lds = Tile<D>::LDS + (BIAS ? (unsigned)p.lds_extra : 0u);
+    if (lds > lds_max) return hipErrorInvalidValue;
     FwdParams pp = p;
     void* args[] = {(void*)&pp};
     return hipLaunchKernel(fn, dim3(p.nblocks), dim3(Tile<D>::NT), args, lds, s);

@@ -29,6 +29,9 @@ __host__ __device__ constexpr int tile_bn(int D) { return D <= 128 ? 64 : 32; }
 __host__ __device__ constexpr int tile_wg_per_cu(int D) { return D <= 128 ? 2 : 1; }
 // K/V tiles loaded ahead of the one being consumed (the LDS ring has one more stage)
 __host__ __device__ constexpr int tile_prefetch(int D) { return D <= 128 ? 1 : 3; }
+// LDS of the K/V ring: (PREFETCH + 1) stages, each a K and a V tile of BN x D 16-bit values
+__host__ __device__ constexpr int tile_ring_bytes(int D) { return (tile_prefetch(D) + 1) * 2 * tile_bn(D) * D * 2; }
+constexpr int kLdsBytesPerCU = 160 * 1024;
 
 struct FwdParams {
     const uint16_t* q;
@@ -37,6 +40,12 @@ struct FwdParams {
     uint16_t* out;
     float* lse;            // may be null
     const uint16_t* bias;  // rel_bias or null
+    // fused rel_bias producer (bias instances, bias == null): r [rows_q, Hq, d_rel] and
+    // rel_proj [d_rel, E]; the work-group's bias rows are built in LDS past the K/V ring
+    const uint16_t* rel_r;
+    const uint16_t* rel_proj;
+    int d_rel;
+    int lds_extra;         // bytes of that LDS region (0 without the fused producer)
     float* o_part;         // split partials (split mode)
     float* lse_part;
     const int* cu_q;       // varlen offsets (varlen mode)

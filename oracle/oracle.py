@@ -154,6 +154,32 @@ def attn_full(*args, **kw):
     return default().attn_full(*args, **kw)
 
 
+def widen16(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """16-bit patterns -> float64 (exact)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return bits.view(np.float16).astype(np.float64)
+
+
+def narrow16(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 -> float32 -> 16-bit patterns, each step rounding to nearest even (the
+    path of a product accumulated in fp32 and stored in the 16-bit dtype)."""
+    x32 = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    if dtype == "bf16":
+        u = x32.view(np.uint32).astype(np.uint64)
+        return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return x32.astype(np.float16).view(np.uint16)
+
+
+def rel_bias_from_proj(r: np.ndarray, rel_proj: np.ndarray, dtype: str) -> np.ndarray:
+    """rel_bias [rows, H, E] = r [rows, H, d_rel] . rel_proj [d_rel, E], the einsum the
+    tml-fa4 page applies before the call, summed in fp64 and stored in the dtype."""
+    rows, H, d_rel = r.shape
+    prod = widen16(r, dtype).reshape(rows * H, d_rel) @ widen16(rel_proj, dtype)
+    return narrow16(prod.reshape(rows, H, rel_proj.shape[1]), dtype)
+
+
 def seq_lengths(B, Sq, Sk, cu_seqlens_q=None, cu_seqlens_k=None, seqused_k=None):
     """Per-batch (q_len, k_len) lists under the oracle's length rules."""
     if cu_seqlens_q is not None:

@@ -91,7 +91,7 @@ class Case:
 
     def __init__(self, *, dtype, B, Sq, Sk, Hq, Hkv, D, Dv=None, scale=None, causal=False,
                  q, k, v, cu_q=None, cu_k=None, max_q=None, max_k=None, seqused=None,
-                 bias=None, num_splits=1, pack_gqa=-1, name="case"):
+                 bias=None, num_splits=1, pack_gqa=-1, name="case", rel_r=None, rel_proj=None):
         self.dtype, self.B, self.Sq, self.Sk = dtype, B, Sq, Sk
         self.Hq, self.Hkv, self.D, self.Dv = Hq, Hkv, D, Dv or D
         self.scale = float(np.float32(scale if scale is not None else 1.0 / math.sqrt(D)))
@@ -100,6 +100,10 @@ class Case:
         self.cu_q, self.cu_k, self.max_q, self.max_k = cu_q, cu_k, max_q, max_k
         self.seqused, self.bias = seqused, bias
         self.num_splits, self.pack_gqa, self.name = num_splits, pack_gqa, name
+        # fused producer: the GPU gets r and rel_proj; the oracle gets the bias they make
+        self.rel_r, self.rel_proj = rel_r, rel_proj
+        if rel_r is not None:
+            self.bias = oracle_mod.rel_bias_from_proj(rel_r, rel_proj, dtype)
 
     @property
     def varlen(self):
@@ -115,7 +119,10 @@ class Case:
                       max_seqlen_q=int(self.max_q), max_seqlen_k=int(self.max_k))
         if self.seqused is not None:
             kw["seqused_k"] = dev_i32(self.seqused)
-        if self.bias is not None:
+        if self.rel_r is not None:
+            kw["rel_r"] = dev16(self.rel_r, self.dtype)
+            kw["rel_proj"] = dev16(self.rel_proj, self.dtype)
+        elif self.bias is not None:
             kw["rel_bias"] = dev16(self.bias, self.dtype)
         q = dev16(self.q, self.dtype)
         k = dev16(self.k, self.dtype)

@@ -388,8 +388,29 @@ def pin_widening(orc):
         assert L[0, 0, 0] == 0.0
 
 
+def pin_rel_proj(orc):
+    """The rel_bias producer (r . rel_proj): torch's float64 einsum stored through
+    float32 into the dtype; a one-hot r picks a row of rel_proj exactly."""
+    from oracle.oracle import rel_bias_from_proj
+    rng = gen.make_rng(1010)
+    for dtype, tdt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+        r = rand_bits(rng, (7, 3, 24), dtype)
+        pj = rand_bits(rng, (24, 128), dtype, 0.2)
+        got = rel_bias_from_proj(r, pj, dtype)
+        ref = torch.einsum("thd,de->the", torch.from_numpy(widen(r, dtype)),
+                           torch.from_numpy(widen(pj, dtype))).to(torch.float32).to(tdt)
+        ref_bits = ref.view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, ref_bits), f"rel_proj product {dtype}"
+        one = np.zeros((2, 1, 24), dtype=np.float32)
+        one[0, 0, 5] = 1.0
+        one[1, 0, 23] = 1.0
+        one_bits = torch.from_numpy(one).to(tdt).view(torch.int16).numpy().view(np.uint16)
+        rows = rel_bias_from_proj(one_bits, pj, dtype)
+        assert np.array_equal(rows[0, 0], pj[5]) and np.array_equal(rows[1, 0], pj[23]), "one-hot r"
+
+
 ALL_PINS = [pin_sdpa_dense, pin_varlen, pin_seqused, pin_rel_bias_sdpa, pin_rel_bias_golden,
-            pin_closed_forms, pin_gqa_repeat, pin_split_combine, pin_widening]
+            pin_closed_forms, pin_gqa_repeat, pin_split_combine, pin_widening, pin_rel_proj]
 
 
 def run_all(orc):

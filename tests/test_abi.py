@@ -177,3 +177,29 @@ def test_python_binding_rejects_bad_dtype():
     x = torch.zeros((1, 4, 1, 64), dtype=torch.float32)
     with pytest.raises(fa.AttnError):
         fa.attn_fwd(x, x, x)
+
+
+def check_rel_proj(lib, r=A, proj=A, d_rel=16, E=256, **over):
+    """attn_fwd_rel_proj with arguments its validation rejects (or B = 0): no GPU call."""
+    a = args(**over)
+    return lib.attn_fwd_rel_proj(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Sq"], a["Sk"],
+                                 a["Hq"], a["Hkv"], a["D"], a["Dv"], a["scale"], a["causal"], a["cu_q"],
+                                 a["cu_k"], a["max_q"], a["max_k"], a["seqused"], r, proj, d_rel, E,
+                                 a["ns"], a["pack"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+def test_rel_proj_validation(lib):
+    C = CODE
+    assert check_rel_proj(lib, B=0) == 0  # nothing to compute
+    assert check_rel_proj(lib, B=0, E=384) == 0
+    assert check_rel_proj(lib, proj=None) == C["ATTN_ERR_NULL_POINTER"]
+    assert check_rel_proj(lib, r=None) == C["ATTN_ERR_NULL_POINTER"]
+    assert check_rel_proj(lib, d_rel=12) == C["ATTN_ERR_BAD_ARG"]
+    assert check_rel_proj(lib, d_rel=0) == C["ATTN_ERR_BAD_ARG"]
+    assert check_rel_proj(lib, d_rel=264) == C["ATTN_ERR_BAD_ARG"]
+    assert check_rel_proj(lib, r=A + 2) == C["ATTN_ERR_MISALIGNED"]
+    assert check_rel_proj(lib, E=100) == C["ATTN_ERR_BAD_REL_EXTENT"]
+    # bias rows of a work-group beside the K/V ring must fit the 160 KB of LDS
+    assert check_rel_proj(lib, E=512) == C["ATTN_ERR_UNSUPPORTED_COMBO"]
+    assert check_rel_proj(lib, D=256, Dv=256, E=256) == C["ATTN_ERR_UNSUPPORTED_COMBO"]
+    assert check_rel_proj(lib, B=0, D=256, Dv=256, E=128) == 0

@@ -31,7 +31,7 @@ def make_case(name, dtype=None, nan_pad=False):
                 cu_q=x.get("cu_seqlens_q"), cu_k=x.get("cu_seqlens_k"),
                 max_q=x.get("max_seqlen_q"), max_k=x.get("max_seqlen_k"), seqused=su,
                 bias=x.get("rel_bias"), num_splits=spec.num_splits, pack_gqa=spec.pack_gqa,
-                name=f"{name} {spec.dtype}")
+                name=f"{name} {spec.dtype}", rel_r=x.get("rel_r"), rel_proj=x.get("rel_proj"))
 
 
 def test_c1_full():
@@ -47,6 +47,11 @@ def test_c2_sampled(dtype):
 def test_c3_sampled():
     c = make_case("c3")
     say(f"  c3 lengths {np.diff(c.cu_q).tolist()}")
+    sampled_check(c, rows=sample_rows(c, max_pairs=10, per_seq_rows=40, tile=64))
+
+
+def test_c3r_fused_bias_sampled():
+    c = make_case("c3r")
     sampled_check(c, rows=sample_rows(c, max_pairs=10, per_seq_rows=40, tile=64))
 
 

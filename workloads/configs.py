@@ -40,6 +40,7 @@ class Spec:
     seqused: Optional[Sequence[int]] = None
     rel_extent: int = 0  # E; 0 = no relative bias
     bias_std: float = 0.5
+    d_rel: int = 0       # > 0: the bias comes as r [rows_q, Hq, d_rel] and rel_proj [d_rel, E]
     num_splits: int = 1  # <= 0: heuristic
     pack_gqa: int = -1   # -1 auto, 0 off, 1 on
     q_std: float = 1.0
@@ -95,7 +96,14 @@ def make_inputs(spec: Spec) -> dict:
     out["q"] = gen.stream_normal_bits(spec.seed, gen.STREAM_Q, qshape, spec.dtype, spec.q_std)
     out["k"] = gen.stream_normal_bits(spec.seed, gen.STREAM_K, kshape, spec.dtype, spec.k_std)
     out["v"] = gen.stream_normal_bits(spec.seed, gen.STREAM_V, vshape, spec.dtype, spec.v_std)
-    if spec.rel_extent:
+    if spec.rel_extent and spec.d_rel:
+        # r ~ N(0, 1), rel_proj ~ N(0, bias_std^2 / d_rel): the product has std bias_std
+        out["rel_r"] = gen.stream_normal_bits(spec.seed, gen.STREAM_REL_R, (nrows_q, spec.Hq, spec.d_rel),
+                                              spec.dtype, 1.0)
+        out["rel_proj"] = gen.stream_normal_bits(spec.seed, gen.STREAM_REL_PROJ,
+                                                 (spec.d_rel, spec.rel_extent), spec.dtype,
+                                                 spec.bias_std / math.sqrt(spec.d_rel))
+    elif spec.rel_extent:
         out["rel_bias"] = gen.stream_normal_bits(spec.seed, gen.STREAM_BIAS,
                                                  (nrows_q, spec.Hq, spec.rel_extent),
                                                  spec.dtype, spec.bias_std)
@@ -112,6 +120,7 @@ def workload(name: str, dtype: Optional[str] = None) -> Spec:
     c4b  fp16 feature attention [100,100000,4,16]
     c4c  fp16 cross attention q[1,1000,6,64] k/v[1,1e6,6,64], split-KV heuristic
     c5a  bf16 D256 8:1 pack-GQA, q[4,1024,8,256], k/v[4,2048,1,256], seqused_k U[600,2048]
+    c3r  c3 with the bias produced in the kernel from r [T,32,16] and rel_proj [16,256]
     c5b  bf16 D256 decode q[32,1,8,256], k/v[32,131072,1,256], causal, split-KV + combine
     n1a/b/c  fp16 cached prediction: q[1,R,8,64] against k/v[1,300000,1,64] (MQA 8:1),
              R = 16 / 64 / 256 query rows, non-causal, split-KV heuristic
@@ -124,6 +133,9 @@ def workload(name: str, dtype: Optional[str] = None) -> Spec:
     if name == "c3":
         return Spec(name, dtype or gen.BF16, 8, 0, 0, 32, 8, 128, 128, True, s128, 3,
                     varlen=True, len_range=(512, 8192), rel_extent=256, bias_std=0.5)
+    if name == "c3r":
+        return Spec(name, dtype or gen.BF16, 8, 0, 0, 32, 8, 128, 128, True, s128, 3,
+                    varlen=True, len_range=(512, 8192), rel_extent=256, bias_std=0.5, d_rel=16)
     if name == "c4a":
         return Spec(name, dtype or gen.FP16, 256, 10000, 10000, 6, 6, 64, 64, False, f32(1 / 8), 41)
     if name == "c4b":
@@ -147,5 +159,5 @@ def workload(name: str, dtype: Optional[str] = None) -> Spec:
 N1_ROWS = {"n1a": 16, "n1b": 64, "n1c": 256}
 N1_SEEDS = {"n1a": 61, "n1b": 62, "n1c": 63}
 
-WORKLOADS = ("c1", "c2", "c3", "c4a", "c4b", "c4c", "c5a", "c5b", "n1a", "n1b", "n1c")
+WORKLOADS = ("c1", "c2", "c3", "c3r", "c4a", "c4b", "c4c", "c5a", "c5b", "n1a", "n1b", "n1c")
 

@@ -30,6 +30,7 @@ _CHUNK = 1 << 22  # float32 draws per chunk of the sequential helper
 BLOCK = 1 << 22   # elements per independently seeded block of a workload tensor
 
 STREAM_META, STREAM_Q, STREAM_K, STREAM_V, STREAM_BIAS = 0, 1, 2, 3, 4
+STREAM_REL_R, STREAM_REL_PROJ = 5, 6  # inputs of the fused rel_bias producer
 
 
 def make_rng(seed: int, stream: int = None, block: int = None) -> np.random.Generator:
