@@ -49,7 +49,10 @@ typedef __attribute__((address_space(3))) s16x4v lds_s16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLoThresh = 32.f;  // rows with a smaller softmax normaliser get the P remainder MFMA
-constexpr float kTau = 8.f;        // O / l are rescaled only when the row max grows by more than 2^kTau
+constexpr float kTau = 8.f;
+// a buffer offset past every range the kernel builds (row bytes x 64 keys stay below it:
+// the host bounds heads x head dim)
+constexpr int kOobOffset = 0x40000000;        // O / l are rescaled only when the row max grows by more than 2^kTau
 
 template <bool BF>
 struct Elem;
@@ -100,6 +103,10 @@ struct Tile {
     static constexpr int PREFETCH = tile_prefetch(D);  // tiles loaded ahead of the one being consumed
     static constexpr int NB = PREFETCH + 1;       // LDS ring stages, each a K tile and a V tile
     static constexpr int WG_PER_CU = tile_wg_per_cu(D);
+    // load offsets and K read addresses formed per tile instead of held in registers
+    // across the key loop: fewer live registers for a few more VALU operations
+    // (measured: faster at head-dim classes 16 and 256, slower at 64 and 128)
+    static constexpr bool LEAN = D == 16 || D == 256;
     static constexpr int LDS = NB * 2 * TILE_BYTES;
     static_assert(LDS == tile_ring_bytes(D), "host and kernel agree on the ring size");
     static constexpr int GRANULES = BN * NG;      // 16-byte granules per tile
@@ -318,21 +325,44 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(((uint64_t)hi << 32) | lo), (short)0, nrec, 0x00020000);
+        // this lane's offset for the first load instruction; where later ones only
+        // add whole rows (the swizzle repeats every key step), they add a scalar
+        constexpr int KSTEP = T::NT / T::NG;  // keys between consecutive instructions of a tile
+        constexpr bool K_ADD = (KSTEP % (T::SWZ_DIV * T::NG)) == 0;
+        int off0;
+        {
+            const int g = 64 * wave + lane;
+            int key, c;
+            if (!is_v) {
+                key = g / T::NG;
+                c = (g % T::NG) ^ ((key / T::SWZ_DIV) % T::NG);
+            } else {
+                key = (g / (4 * T::NG)) * 4 + (g & 3);
+                c = (g >> 2) % T::NG;
+            }
+            // columns past D (Dv): an offset past any range, so the load writes zeros
+            off0 = c < ng ? key * row_bytes + c * 16 : kOobOffset;
+        }
+        if (T::LEAN) asm volatile("" : "+v"(off0));  // formed per tile, not held across the loop
 #pragma unroll
         for (int u = 0; u < T::LOADS; u++) {
             const int g0 = T::NT * u + 64 * wave;  // first granule of this wave's instruction
             if (T::GRANULES % T::NT == 0 || g0 < T::GRANULES) {
-                const int g = g0 + lane;
-                int key, c;
-                if (!is_v) {
-                    key = g / T::NG;
-                    c = (g % T::NG) ^ ((key / T::SWZ_DIV) % T::NG);
+                int off;
+                if (T::LEAN && (is_v || K_ADD)) {
+                    off = off0 + u * KSTEP * row_bytes;
                 } else {
-                    key = (g / (4 * T::NG)) * 4 + (g & 3);
-                    c = (g >> 2) % T::NG;
+                    const int g = g0 + lane;
+                    int key, c;
+                    if (!is_v) {
+                        key = g / T::NG;
+                        c = (g % T::NG) ^ ((key / T::SWZ_DIV) % T::NG);
+                    } else {
+                        key = (g / (4 * T::NG)) * 4 + (g & 3);
+                        c = (g >> 2) % T::NG;
+                    }
+                    off = c < ng ? key * row_bytes + c * 16 : (T::LEAN ? kOobOffset : nrec);
                 }
-                // columns past D (Dv): an offset past the range, so the load writes zeros
-                const int off = c < ng ? key * row_bytes + c * 16 : nrec;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + g0 * 16), 16, off, 0, 0, 0);
             }
         }
@@ -348,13 +378,19 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
                 for (int r = 0; r < 16; r++) s[qb][kb2][r] = 0.f;
 #pragma unroll
         for (int kb2 = 0; kb2 < T::NKB; kb2++) {
-            const int key = kb2 * 32 + l32;
+            // the swizzle puts granule 2c + hf of a key at (granule hf) ^ 2c, so the
+            // byte offsets of a lane's reads differ by an XOR with 32c from the first
+            int a0 = k_granule<D>(l32, hf) * 16;
+            if (T::LEAN) asm volatile("" : "+v"(a0));  // formed per tile, not held across the loop
+            const char* base = kl + kb2 * 32 * T::NG * 16;
             // all reads of a 32-key block go out before its MFMAs (the compiler
             // barrier keeps them from being sunk back to their uses), so each MFMA
             // finds its operand landed instead of waiting out the LDS latency
             v8 ka[T::NC];
 #pragma unroll
-            for (int c = 0; c < T::NC; c++) ka[c] = *(const v8*)(kl + k_granule<D>(key, 2 * c + hf) * 16);
+            for (int c = 0; c < T::NC; c++)
+                ka[c] = T::LEAN ? *(const v8*)(base + (a0 ^ (32 * c)))
+                                : *(const v8*)(kl + k_granule<D>(kb2 * 32 + l32, 2 * c + hf) * 16);
             asm volatile("" ::: "memory");
 #pragma unroll
             for (int c = 0; c < T::NC; c++)
