@@ -361,7 +361,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
                         key = (g / (4 * T::NG)) * 4 + (g & 3);
                         c = (g >> 2) % T::NG;
                     }
-                    off = c < ng ? key * row_bytes + c * 16 : (T::LEAN ? kOobOffset : nrec);
+                    off = c < ng ? key * row_bytes + c * 16 : kOobOffset;
                 }
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + g0 * 16), 16, off, 0, 0, 0);
             }
