@@ -70,6 +70,7 @@ struct Elem<true> {  // bfloat16
         return __builtin_bit_cast(uint16_t, (__bf16)x);
     }
     static __device__ __forceinline__ __bf16 to_elem(float x) { return (__bf16)x; }
+    static constexpr uint16_t kNegInfBits = 0xFF80;
 };
 
 template <>
@@ -85,6 +86,7 @@ struct Elem<false> {  // IEEE half
         return __builtin_bit_cast(uint16_t, (_Float16)x);
     }
     static __device__ __forceinline__ _Float16 to_elem(float x) { return (_Float16)x; }
+    static constexpr uint16_t kNegInfBits = 0xFC00;
 };
 
 template <int D>
@@ -485,8 +487,8 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     // in phase 2 rather than kept in registers across the rescale.
     // The bias of a band tile is read once, at the start of the tile step and
     // before that step's K/V prefetch goes out (waiting for these loads then does
-    // not wait for the prefetch), into 16-bit pairs; elements outside the band or
-    // not visible hold 0.
+    // not wait for the prefetch), into 16-bit pairs, with the mask folded in:
+    // visible elements outside the band hold 0, masked ones the dtype's -inf.
     typedef uint32_t BiasBits[T::NQB][T::NKB][8];
     auto bias_row = [&](int qb) __attribute__((always_inline)) {
         return BIAS ? p.bias + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)p.E : nullptr;
@@ -510,7 +512,9 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
                         const int j = j0 + kb2 * 32 + acc_row(2 * r2 + e, hf);
                         const int d = i + delta - j;
                         const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
-                        if (vis && qvalid[qb] && d >= 0 && d < p.E) w |= (uint32_t)brow[d] << (16 * e);
+                        uint32_t h = vis ? 0u : (uint32_t)E::kNegInfBits;  // masked: the -inf of the dtype
+                        if (vis && qvalid[qb] && d >= 0 && d < p.E) h = brow[d];
+                        w |= h << (16 * e);
                     }
                     bb[qb][kb2][r2] = w;
                 }
@@ -518,12 +522,13 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     };
     auto slow_term = [&](int qb, int kb2, int r, int j0, bool band, const BiasBits& bb)
         __attribute__((always_inline)) {
+        // a band tile's terms were formed with the mask folded in (masked keys hold
+        // -inf); other tiles work the mask out here
+        if (BIAS && band) return E::widen((uint16_t)(bb[qb][kb2][r >> 1] >> (16 * (r & 1)))) * kLog2e;
         const int i = qi[qb];
         const int j = j0 + kb2 * 32 + acc_row(r, hf);
         const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
-        float b2 = 0.f;
-        if (BIAS && band) b2 = E::widen((uint16_t)(bb[qb][kb2][r >> 1] >> (16 * (r & 1)))) * kLog2e;
-        return vis ? b2 : -INFINITY;  // -inf marks a masked key
+        return vis ? 0.f : -INFINITY;  // -inf marks a masked key
     };
     auto max_slow = [&](STile& s, int j0, bool band, const BiasBits& bb) __attribute__((always_inline)) {
         // opaque copy: keeps the per-element key indices inside the slow path
