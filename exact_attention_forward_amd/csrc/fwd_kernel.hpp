@@ -496,11 +496,13 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     // fused producer: the bias rows of the work-group, [BM][E], built in LDS
     const bool fused_bias = BIAS && p.rel_r != nullptr;
     uint16_t* bias_lds = (uint16_t*)(smem + T::LDS);
-    auto load_bias = [&](BiasBits& bb, int j0) __attribute__((always_inline)) {
+    // Every element reads its bias at a clamped index (inside the row) and the band
+    // test selects with bit masks, so each read is used whatever the test gives:
+    // the reads need no branches and go out together.
+    auto load_bias_from = [&](BiasBits& bb, int j0, auto row_of) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
-            const uint16_t* brow = fused_bias ? bias_lds + ((wave * T::NQB + qb) * 32 + l32) * p.E
-                                              : bias_row(qb);
+            const auto brow = row_of(qb);
             const int i = qi[qb];
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
@@ -511,14 +513,82 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
                     for (int e = 0; e < 2; e++) {
                         const int j = j0 + kb2 * 32 + acc_row(2 * r2 + e, hf);
                         const int d = i + delta - j;
+                        const uint32_t v = brow[min(max(d, 0), p.E - 1)];
                         const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
-                        uint32_t h = vis ? 0u : (uint32_t)E::kNegInfBits;  // masked: the -inf of the dtype
-                        if (vis && qvalid[qb] && d >= 0 && d < p.E) h = brow[d];
+                        const bool keep = vis && qvalid[qb] && d >= 0 && d < p.E;
+                        // masked: the -inf of the dtype; visible outside the band: 0
+                        const uint32_t h = (v & (keep ? 0xFFFFu : 0u)) | (vis ? 0u : (uint32_t)E::kNegInfBits);
                         w |= h << (16 * e);
                     }
                     bb[qb][kb2][r2] = w;
                 }
         }
+    };
+    // From HBM: one buffer read per element, all at one per-lane offset plus an
+    // immediate. Within a lane the d of a tile's elements fall in a window of
+    // CMAX + 1 values below d0, and over the lanes of a band tile d0 >= -35, so
+    // with the descriptor starting one bias row before the wave's first row
+    // (first >= 1) every offset is positive; a read that leaves the tensor returns
+    // 0 (such elements lie outside the band). Otherwise (the wave holds the
+    // tensor's first row, or a wave's rows span more than 2^31 bytes of bias) the
+    // reads take clamped indices.
+    auto load_bias_global = [&](BiasBits& bb, int j0, long long base_row) __attribute__((always_inline)) {
+        constexpr int CMAX = (T::NKB - 1) * 32 + 27;  // largest key offset within the tile, less 4hf
+        const char* base = (const char*)p.bias + base_row * p.E * 2;
+        const long long left = ((long long)p.rows_q * p.Hq - base_row) * p.E * 2;
+        const int nrec = __builtin_amdgcn_readfirstlane((int)min(left, (long long)INT32_MAX));
+        const uint64_t addr = (uint64_t)base;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(((uint64_t)hi << 32) | lo), (short)0, nrec, 0x00020000);
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) {
+            const int i = qi[qb];
+            const long long row = (q_off + i) * p.Hq + qh[qb];
+            const int d0 = i + delta - j0 - 4 * hf;  // d of element (kb2, r) is d0 - c(kb2, r)
+            const int vo = (int)((row - base_row) * p.E + d0 - CMAX) * 2;
+            uint32_t raw[T::NKB][16];
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int c = kb2 * 32 + 8 * (r >> 2) + (r & 3);
+                    raw[kb2][r] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, vo + 2 * (CMAX - c), 0, 0);
+                }
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++)
+#pragma unroll
+                for (int r2 = 0; r2 < 8; r2++) {
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int e = 0; e < 2; e++) {
+                        const int j = j0 + kb2 * 32 + acc_row(2 * r2 + e, hf);
+                        const int d = i + delta - j;
+                        const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
+                        const bool keep = vis && qvalid[qb] && d >= 0 && d < p.E;
+                        // masked: the -inf of the dtype; visible outside the band: 0
+                        const uint32_t h = (raw[kb2][2 * r2 + e] & (keep ? 0xFFFFu : 0u)) |
+                                           (vis ? 0u : (uint32_t)E::kNegInfBits);
+                        w |= h << (16 * e);
+                    }
+                    bb[qb][kb2][r2] = w;
+                }
+        }
+    };
+    // the wave's first bias row (a lower bound over its lanes; uniform)
+    long long bias_first_row = (q_off + min(w_row, r_last) / gp) * p.Hq + h_base;
+    bias_first_row = (long long)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)bias_first_row >> 32)) << 32) |
+                                 __builtin_amdgcn_readfirstlane((uint32_t)bias_first_row));
+    auto load_bias = [&](BiasBits& bb, int j0) __attribute__((always_inline)) {
+        if (fused_bias)
+            load_bias_from(bb, j0, [&](int qb) {
+                return (const __attribute__((address_space(3))) uint16_t*)(bias_lds + ((wave * T::NQB + qb) * 32 + l32) * p.E);
+            });
+        else if (bias_first_row >= 1 && (long long)(T::BM + 2) * p.Hq * p.E * 2 < INT32_MAX)
+            load_bias_global(bb, j0, bias_first_row - 1);  // (offsets fit 31 bits)
+        else
+            load_bias_from(bb, j0, [&](int qb) { return bias_row(qb); });
     };
     auto slow_term = [&](int qb, int kb2, int r, int j0, bool band, const BiasBits& bb)
         __attribute__((always_inline)) {
