@@ -193,20 +193,20 @@ size_t attn_fwd_workspace_size(int B, int Sq, int Hq, int Dv, int is_varlen, int
 
 namespace {
 
-// LDS the fused producer needs for the bias rows of one work-group: BM rows x E values
-long long rel_rows_lds_bytes(int dclass, int rel_extent) {
-    return (long long)tile_bm(dclass) * rel_extent * 2;
+// LDS the fused producer needs past the K/V ring: one key tile's bias values for each
+// of the work-group's BM rows (BM x BN x 2 bytes, whatever rel_extent is)
+long long rel_rows_lds_bytes(int dclass) {
+    return (long long)tile_bm(dclass) * tile_bn(dclass) * 2;
 }
 
 // The fused-producer arguments on top of validate(): r and rel_proj given, d_rel a
-// multiple of 8 in [8, 256], r 16-byte aligned, and the bias rows fitting in LDS.
-attn_status_t validate_rel_proj(const void* rel_r, const void* rel_proj, int d_rel, int rel_extent,
-                                const Plan& pl) {
+// multiple of 8 in [8, 256], r 16-byte aligned.
+attn_status_t validate_rel_proj(const void* rel_r, const void* rel_proj, int d_rel, const Plan& pl) {
     if (!rel_r || !rel_proj) return ATTN_ERR_NULL_POINTER;
     if (d_rel < 8 || d_rel > 256 || d_rel % 8) return ATTN_ERR_BAD_ARG;
     if (!is_aligned(rel_r, 16) || !is_aligned(rel_proj, 2)) return ATTN_ERR_MISALIGNED;
-    if (tile_ring_bytes(pl.dclass) + rel_rows_lds_bytes(pl.dclass, rel_extent) > kLdsBytesPerCU)
-        return ATTN_ERR_UNSUPPORTED_COMBO;
+    if (tile_ring_bytes(pl.dclass) + rel_rows_lds_bytes(pl.dclass) > kLdsBytesPerCU / tile_wg_per_cu(pl.dclass))
+        return ATTN_ERR_UNSUPPORTED_COMBO;  // (never: the ring and this region fit beside each other)
     return ATTN_OK;
 }
 
@@ -251,7 +251,7 @@ attn_status_t attn_fwd_rel_proj(const void* q, const void* k, const void* v, voi
                  max_seqlen_q, max_seqlen_k, rel_r ? rel_r : rel_proj, rel_extent, num_splits, pack_gqa,
                  dtype, workspace, workspace_bytes, pl);
     if (st != ATTN_OK) return st;
-    st = validate_rel_proj(rel_r, rel_proj, d_rel, rel_extent, pl);
+    st = validate_rel_proj(rel_r, rel_proj, d_rel, pl);
     if (st != ATTN_OK) return st;
     if (pl.nblocks == 0) return ATTN_OK;
     return run_fwd(pl, q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, Dv, scale, causal, cu_seqlens_q,
@@ -278,7 +278,7 @@ attn_status_t run_fwd(const Plan& pl, const void* q, const void* k, const void* 
     p.rel_r = (const uint16_t*)rel_r;
     p.rel_proj = (const uint16_t*)rel_proj;
     p.d_rel = d_rel;
-    p.lds_extra = rel_r ? (int)rel_rows_lds_bytes(pl.dclass, rel_extent) : 0;
+    p.lds_extra = rel_r ? (int)rel_rows_lds_bytes(pl.dclass) : 0;
     p.o_part = nullptr;
     p.lse_part = nullptr;
     if (pl.ns > 1) {

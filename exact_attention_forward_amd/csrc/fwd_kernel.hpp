@@ -493,7 +493,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     auto bias_row = [&](int qb) __attribute__((always_inline)) {
         return BIAS ? p.bias + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)p.E : nullptr;
     };
-    // fused producer: the bias rows of the work-group, [BM][E], built in LDS
+    // fused producer: per band tile, each wave's bias values in LDS past the ring (32 rows x BN)
     const bool fused_bias = BIAS && p.rel_r != nullptr;
     uint16_t* bias_lds = (uint16_t*)(smem + T::LDS);
     // Every element reads its bias at a clamped index (inside the row) and the band
@@ -580,11 +580,95 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     long long bias_first_row = (q_off + min(w_row, r_last) / gp) * p.Hq + h_base;
     bias_first_row = (long long)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)bias_first_row >> 32)) << 32) |
                                  __builtin_amdgcn_readfirstlane((uint32_t)bias_first_row));
+    // Fused producer (tml-fa4 page: rel_bias = r . rel_proj, the einsum over d_rel), per
+    // band tile and wave. Over the wave's rows the tile needs d in [dbase, dbase + BN + 31)
+    // with dbase = wi_lo + delta - j0 - (BN - 1); the MFMA forms C[d][row] = rel_proj^T r^T
+    // for that range in 32-d blocks (A = a rel_proj column per lane, zero outside [0, E);
+    // B = the lane's r row), so each lane ends up holding values of its own row. Rounded
+    // to the dtype (as a materialised rel_bias is), they go to the row's LDS slot of BN
+    // values, slot u holding d = dbase + (row - wi_lo) + u: the first and the last block
+    // share the slots (u = (m - off) mod BN takes the first block's value for m >= off,
+    // the last one's below), the blocks between fill theirs whole, so every write is
+    // unconditional. The tile's elements then read their d at a fixed u per element.
+    auto produce_bias = [&](BiasBits& bb, int j0) __attribute__((always_inline)) {
+        static_assert(T::NQB == 1, "one 32-row block per wave");
+        constexpr int NBLK = T::NKB + 1;  // 32-d blocks covering BN + 31 values
+        const int dbase = wi_lo + delta - j0 - (T::BN - 1);
+        const int i = qi[0];
+        const int off = i - wi_lo;  // 0 .. 31
+        uint16_t* slot = bias_lds + (wave * 32 + l32) * T::BN;
+        // opaque copies: the addresses below are formed per tile instead of being
+        // hoisted out of the key loop into registers held across it
+        int E_ = p.E, drel = p.d_rel;
+        asm volatile("" : "+s"(E_), "+s"(drel));
+        const uint16_t* rrow = p.rel_r + ((q_off + i) * p.Hq + qh[0]) * (long long)drel;
+        const uint16_t* proj = p.rel_proj;
+        auto block = [&](int b) __attribute__((always_inline)) {
+            f32x16 c = {};
+            const int dcol = dbase + 32 * b + l32;  // the A row (d) this lane provides
+            const bool din = dcol >= 0 && dcol < E_;
+            const uint16_t* pcol = proj + min(max(dcol, 0), E_ - 1);
+            for (int k0 = 0; k0 < drel; k0 += 16) {
+                const int ka = k0 + 8 * hf;  // this lane's 8 contraction indices
+                u32x4 bw = {0u, 0u, 0u, 0u};
+                if (ka < drel) bw = *(const u32x4*)(rrow + ka);
+                u32x4 aw = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const int k1 = min(ka + e, drel - 1), k2 = min(ka + e + 1, drel - 1);
+                    const uint32_t v1 = pcol[k1 * E_];
+                    const uint32_t v2 = pcol[k2 * E_];
+                    const uint32_t keep1 = din && ka + e < drel ? 0xFFFFu : 0u;
+                    const uint32_t keep2 = din && ka + e + 1 < drel ? 0xFFFFu : 0u;
+                    aw[e >> 1] = (v1 & keep1) | ((v2 & keep2) << 16);
+                }
+                c = E::mma(__builtin_bit_cast(v8, aw), __builtin_bit_cast(v8, bw), c);
+            }
+            return c;
+        };
+        {
+            const f32x16 cf = block(0), cl = block(NBLK - 1);
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = acc_row(r, hf);
+                slot[(m - off) & (T::BN - 1)] = E::narrow(m >= off ? cf[r] : cl[r]);
+            }
+        }
+#pragma unroll
+        for (int b = 1; b < NBLK - 1; b++) {
+            const f32x16 c = block(b);
+#pragma unroll
+            for (int r = 0; r < 16; r++) slot[32 * b + acc_row(r, hf) - off] = E::narrow(c[r]);
+        }
+        // element (kb2, r) of the lane: u = BN - 1 - kb2 * 32 - acc_row(r, hf); a group of
+        // four (r = 4g .. 4g + 3) is one aligned 8-byte read, its values in reverse order
+#pragma unroll
+        for (int kb2 = 0; kb2 < T::NKB; kb2++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int u_lo = T::BN - 4 - kb2 * 32 - 8 * g - 4 * hf;
+                const u32x2 x = *(const u32x2*)(slot + u_lo);
+                const uint32_t pr[2] = {__builtin_amdgcn_alignbit(x[1], x[1], 16),  // elements 4g, 4g + 1
+                                        __builtin_amdgcn_alignbit(x[0], x[0], 16)}; // elements 4g + 2, 4g + 3
+#pragma unroll
+                for (int h2 = 0; h2 < 2; h2++) {
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int e = 0; e < 2; e++) {
+                        const int r = 4 * g + 2 * h2 + e;
+                        const int j = j0 + kb2 * 32 + acc_row(r, hf);
+                        const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
+                        const uint32_t v = (pr[h2] >> (16 * e)) & 0xFFFFu;
+                        // masked: the -inf of the dtype; values outside [0, E) came out 0
+                        w |= (vis ? v : (uint32_t)E::kNegInfBits) << (16 * e);
+                    }
+                    bb[0][kb2][2 * g + h2] = w;
+                }
+            }
+    };
     auto load_bias = [&](BiasBits& bb, int j0) __attribute__((always_inline)) {
         if (fused_bias)
-            load_bias_from(bb, j0, [&](int qb) {
-                return (const __attribute__((address_space(3))) uint16_t*)(bias_lds + ((wave * T::NQB + qb) * 32 + l32) * p.E);
-            });
+            produce_bias(bb, j0);
         else if (bias_first_row >= 1 && (long long)(T::BM + 2) * p.Hq * p.E * 2 < INT32_MAX)
             load_bias_global(bb, j0, bias_first_row - 1);  // (offsets fit 31 bits)
         else
@@ -779,35 +863,6 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         __syncthreads();
     };
     if (kb_begin < kb_end) {
-        if (fused_bias) {
-            // tml-fa4 page: rel_bias = r . rel_proj (the einsum over d_rel). Each wave builds
-            // the rows of its queries: C[32 rows x 32 d] = R[32 x d_rel] . rel_proj[d_rel x 32]
-            // on the MFMA (A = the lane's r row, B = a rel_proj column block), rounded to
-            // the input dtype as a materialised rel_bias would be, into LDS.
-#pragma unroll
-            for (int qb = 0; qb < T::NQB; qb++) {
-                const uint16_t* rrow = p.rel_r + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)p.d_rel;
-                uint16_t* out_rows = bias_lds + (wave * T::NQB + qb) * 32 * p.E;
-                for (int db = 0; db < p.E / 32; db++) {
-                    f32x16 c = {};
-                    for (int k0 = 0; k0 < p.d_rel; k0 += 16) {
-                        const int ka = k0 + 8 * hf;  // this lane's 8 contraction indices
-                        u32x4 a = {0u, 0u, 0u, 0u};
-                        if (qvalid[qb] && ka < p.d_rel) a = *(const u32x4*)(rrow + ka);
-                        u32x4 bw = {0u, 0u, 0u, 0u};
-                        if (ka < p.d_rel) {
-                            const uint16_t* pc = p.rel_proj + (long long)ka * p.E + 32 * db + l32;
-#pragma unroll
-                            for (int e = 0; e < 8; e += 2)
-                                bw[e >> 1] = (uint32_t)pc[e * p.E] | ((uint32_t)pc[(e + 1) * p.E] << 16);
-                        }
-                        c = E::mma(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, bw), c);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 16; r++) out_rows[acc_row(r, hf) * p.E + 32 * db + l32] = E::narrow(c[r]);
-                }
-            }
-        }
         const int first_end = min(kb_begin + T::PREFETCH, kb_end);
         for (int j = kb_begin; j < first_end; j++) issue(j, j - kb_begin);
         wait_tiles_after_next(first_end - 1 - kb_begin);  // tile kb_begin has landed

@@ -124,17 +124,16 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
  *
  * The tml-fa4 page builds rel_bias as the product of r [total_q, n_q_heads, d_rel]
  * (flattened like q) with rel_proj [d_rel, rel_extent] (an einsum over d_rel) before
- * the call. Here the product is formed per work-group on the MFMA and kept in LDS, so
- * the [rows_q, Hq, rel_extent] tensor is never written to or read from HBM:
+ * the call. Here the values each key tile of the band needs are formed on the MFMA
+ * inside the kernel and kept in LDS, so the [rows_q, Hq, rel_extent] tensor is never
+ * written to or read from HBM:
  *   rel_bias[t, h, d] = round_to_dtype( sum_e r[t, h, e] * rel_proj[e, d] )
  * with the sum in fp32 and the rounding to `dtype` (nearest even) that a rel_bias
  * materialised in q's dtype has; everything else is attn_fwd with that rel_bias.
  * r: [rows_q, Hq, d_rel] of `dtype`, device, 16-byte aligned; rel_proj: [d_rel,
  * rel_extent] of `dtype`, device. d_rel: a multiple of 8 in [8, 256]. rel_extent as
- * for attn_fwd (a positive multiple of 128). The bias rows of one work-group
- * (128 rows x rel_extent x 2 bytes) must fit in the 160 KB of LDS beside the K/V
- * ring (64 KB for max(D, Dv) in 65..128, 128 KB above): rel_extent <= 384 there,
- * <= 128 above 128; otherwise ATTN_ERR_UNSUPPORTED_COMBO. Other arguments, errors and ownership as attn_fwd
+ * for attn_fwd (a positive multiple of 128), with no further limit. Other arguments,
+ * errors and ownership as attn_fwd
  * (r stands in for rel_bias in the NULL / alignment checks; a missing rel_proj is
  * ATTN_ERR_NULL_POINTER, a bad d_rel ATTN_ERR_BAD_ARG).
  */

@@ -43,6 +43,8 @@ def case(seed, *, dtype, qls, kls, Hq, Hkv, D, Dv, d_rel, E, causal, num_splits=
     ("bf16", 72, 48, 64, 128, False, 1),
     ("fp16", 16, 16, 24, 256, True, 0),
     ("bf16", 256, 256, 16, 128, True, 1),
+    ("bf16", 128, 128, 16, 512, True, 1),
+    ("fp16", 256, 200, 32, 384, False, 1),
 ])
 def test_fused_bias_matches_oracle_and_materialised(dtype, D, Dv, d_rel, E, causal, splits):
     c = case(8100 + D + d_rel + E, dtype=dtype, qls=[300, 0, 130, 517], kls=[300, 40, 200, 517],
