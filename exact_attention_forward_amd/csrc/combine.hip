@@ -40,7 +40,7 @@ __device__ __forceinline__ uint16_t narrow(float x) {
 template <int DV, bool BF>
 __global__ void __launch_bounds__(256) attn_combine_kernel(const CombineParams p) {
     constexpr int PER = DV >= 64 ? DV / 64 : 1;  // columns per lane
-    constexpr int UNROLL = 4;                     // splits per wave in flight
+    constexpr int UNROLL = 16 / PER;              // splits per wave in flight (16 loads per lane)
     __shared__ float red[4];
     __shared__ float part[4][DV];
     const int tid = threadIdx.x;
