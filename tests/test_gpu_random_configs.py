@@ -17,7 +17,7 @@ from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 96
 
 
 @pytest.fixture(scope="module", autouse=True)
