@@ -20,10 +20,9 @@
 //     ds_read_b64_tr_b16 out of a 4x4-blocked V layout, so each 16-lane group
 //     reads 128 contiguous bytes. Every O^T register of a lane belongs to one
 //     query, so the online-softmax rescale is a per-lane scalar multiply.
-//   * K/V tiles of BN keys (64 up to head dim 128, 32 at 256) sit in an LDS
-//     ring of PREFETCH + 1 stages (2 stages up to head dim 128, 4 at 256); the
-//     loads of the next PREFETCH tiles are in flight while a tile is computed;
-//     one barrier per tile.
+//   * K/V tiles of BN = 64 keys sit in an LDS ring of PREFETCH + 1 = 2 stages;
+//     the loads of the next tile are in flight while a tile is computed; one
+//     barrier per tile.
 //   * Only tiles that cross the key bound, the causal diagonal or the bias band
 //     run the per-element mask / bias code.
 #pragma once

@@ -152,8 +152,8 @@ BM = 128  # rows per work-group of the forward kernel
 
 
 def bn(D):
-    """Keys per key block of the forward kernel: 64 up to head dim 128, 32 above."""
-    return 64 if D <= 128 else 32
+    """Keys per key block of the forward kernel: 64 at every head dim."""
+    return 64
 
 
 def ceil_div(a, b):

@@ -2,8 +2,8 @@
 
 The kernel reads a band tile's bias with one per-lane offset plus immediates and
 builds the fused producer's values in a per-row LDS slot; both lean on bounds of
-its row / key geometry (a 128-row work-group of four 32-row waves, 64-key tiles up
-to head-dim class 128 and 32-key tiles above, bottom-right causal mask, the band
+its row / key geometry (a 128-row work-group of four 32-row waves, 64-key tiles
+(32-key tiles checked as well), bottom-right causal mask, the band
 0 <= d < E with d = i + (k_len - q_len) - j). This walks that geometry for random
 shapes and checks the bounds:
 
