@@ -20,9 +20,9 @@
 //     ds_read_b64_tr_b16 out of a 4x4-blocked V layout, so each 16-lane group
 //     reads 128 contiguous bytes. Every O^T register of a lane belongs to one
 //     query, so the online-softmax rescale is a per-lane scalar multiply.
-//   * K/V tiles of BN = 64 keys sit in an LDS ring of PREFETCH + 1 = 2 stages;
-//     the loads of the next tile are in flight while a tile is computed; one
-//     barrier per tile.
+//   * K/V tiles of BN keys (64; 128 at head-dim class 16) sit in an LDS ring of
+//     PREFETCH + 1 = 2 stages; the loads of the next tile are in flight while a
+//     tile is computed; one barrier per tile.
 //   * Only tiles that cross the key bound, the causal diagonal or the bias band
 //     run the per-element mask / bias code.
 #pragma once
@@ -668,7 +668,8 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     auto load_bias = [&](BiasBits& bb, int j0) __attribute__((always_inline)) {
         if (fused_bias)
             produce_bias(bb, j0);
-        else if (bias_first_row >= 1 && (long long)(T::BM + 2) * p.Hq * p.E * 2 < INT32_MAX)
+        else if (bias_first_row >= 1 && p.E > (T::NKB - 1) * 32 + 27 + 35 &&
+                 (long long)(T::BM + 2) * p.Hq * p.E * 2 < INT32_MAX)
             load_bias_global(bb, j0, bias_first_row - 1);  // (offsets fit 31 bits)
         else
             load_bias_from(bb, j0, [&](int qb) { return bias_row(qb); });

@@ -23,12 +23,14 @@ struct TileGeom {
 
 __host__ __device__ constexpr int tile_nqb(int /*D*/) { return 1; }
 __host__ __device__ constexpr int tile_bm(int D) { return 4 * 32 * tile_nqb(D); }
-__host__ __device__ constexpr int tile_bn(int /*D*/) { return 64; }
+// Keys per K/V tile: 64; 128 at head-dim class 16, where a tile's MFMA work is smallest
+// (measured c4b -6% time against 64; at class 64 the same measured +3% on c4a).
+__host__ __device__ constexpr int tile_bn(int D) { return D <= 16 ? 128 : 64; }
 // Work-groups resident per CU: two up to head dim 128; at 256 a wave needs more
 // than 256 registers, so one.
 __host__ __device__ constexpr int tile_wg_per_cu(int D) { return D <= 128 ? 2 : 1; }
 // K/V tiles loaded ahead of the one being consumed (the LDS ring has one more stage):
-// one, in a ring of 64 KB up to head dim 128 and 128 KB at 256 (measured at 256
+// one, in a ring of at most 64 KB up to head dim 128 and 128 KB at 256 (measured at 256
 // against 32-key tiles three ahead: prefill c5a -16%, decode c5b -10% time)
 __host__ __device__ constexpr int tile_prefetch(int /*D*/) { return 1; }
 // LDS of the K/V ring: (PREFETCH + 1) stages, each a K and a V tile of BN x D 16-bit values

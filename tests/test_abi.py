@@ -152,8 +152,8 @@ BM = 128  # rows per work-group of the forward kernel
 
 
 def bn(D):
-    """Keys per key block of the forward kernel: 64 at every head dim."""
-    return 64
+    """Keys per key block of the forward kernel: 128 at head-dim class 16, 64 above."""
+    return 128 if D <= 16 else 64
 
 
 def ceil_div(a, b):
