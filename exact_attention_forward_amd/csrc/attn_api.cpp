@@ -80,8 +80,15 @@ bool make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_var
     } else if (base == 0 || base >= (long long)kNumCUs * tile_wg_per_cu(dc)) {
         ns = 1;
     } else {
-        // one wave of resident work-groups: CUs x work-groups per CU
+        // one wave of resident work-groups: CUs x work-groups per CU; then up to 8 such
+        // waves while each split keeps at least 64 key blocks (the tail of the last
+        // wave weighs less; measured c4c -12%, n1c -5% time against one wave)
         ns = (int)((long long)kNumCUs * tile_wg_per_cu(dc) / base);
+        if (ns >= 1) {
+            long long rounds = (long long)pl.nkb_max / ns / 64;
+            if (rounds > 8) rounds = 8;
+            if (rounds > 1) ns = (int)(ns * rounds);
+        }
         const int cap = pl.nkb_max / 4 > 0 ? pl.nkb_max / 4 : 1;
         if (ns > cap) ns = cap;
         if (ns > ATTN_MAX_SPLITS) ns = ATTN_MAX_SPLITS;

@@ -166,9 +166,10 @@ attn_status_t attn_check_args(const void* q, const void* k, const void* v, void*
  * Pure host function. Returns >= 1, or 0 for invalid sizes.
  * Heuristic: split only when the unsplit grid has fewer work-groups than fit
  * on the chip at once (256 compute units x 2 work-groups each for D <= 128,
- * x 1 for D = 256); then use floor(that / work-groups) splits (one wave of
- * work-groups fills the chip), never fewer than 4 key blocks per split (64 keys
- * per block for D <= 128, 32 for D = 256).
+ * x 1 for D = 256); then use n = floor(that / work-groups) splits (one wave of
+ * work-groups fills the chip), times r = min(8, floor(key blocks / n / 64)) when
+ * r > 1 (several waves while each split keeps at least 64 key blocks), never
+ * fewer than 4 key blocks per split (64 keys per block; 128 for D <= 16).
  */
 int attn_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_varlen,
                     int max_seqlen_q, int max_seqlen_k, int pack_gqa, int num_splits);

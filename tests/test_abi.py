@@ -166,10 +166,16 @@ def resident(D):
 
 
 def heuristic(work_groups, k_len, D):
-    """The documented split rule: floor(resident / work-groups), at least 4 key blocks per split."""
+    """The documented split rule: floor(resident / work-groups), times up to 8 waves while each
+    split keeps 64 key blocks, at least 4 key blocks per split."""
     if work_groups >= resident(D):
         return 1
-    return max(1, min(resident(D) // work_groups, max(1, ceil_div(k_len, bn(D)) // 4), 256))
+    nkb = ceil_div(k_len, bn(D))
+    n = resident(D) // work_groups
+    rounds = min(8, nkb // n // 64)
+    if rounds > 1:
+        n *= rounds
+    return max(1, min(n, max(1, nkb // 4), 256))
 
 
 def test_python_binding_rejects_bad_dtype():
