@@ -12,14 +12,9 @@ __host__ __device__ constexpr int head_dim_class(int d) {
     return d <= 16 ? 16 : d <= 64 ? 64 : d <= 128 ? 128 : 256;
 }
 
-// Work-group geometry of the forward kernel for head-dim class D.
-//   4 waves of 64 lanes; each wave owns NQB blocks of 32 query rows
-//   (one MFMA 32x32 output column block per row block); BN keys per K/V tile.
-struct TileGeom {
-    int nqb;   // 32-row blocks per wave
-    int bm;    // rows per work-group = 4 * 32 * nqb
-    int bn;    // keys per K/V tile
-};
+// Work-group geometry of the forward kernel for head-dim class D: 4 waves of 64
+// lanes; each wave owns NQB blocks of 32 query rows (one MFMA 32x32 output column
+// block per row block); BN keys per K/V tile.
 
 __host__ __device__ constexpr int tile_nqb(int /*D*/) { return 1; }
 __host__ __device__ constexpr int tile_bm(int D) { return 4 * 32 * tile_nqb(D); }
