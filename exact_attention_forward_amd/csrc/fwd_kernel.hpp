@@ -482,13 +482,30 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     // Tiles that cross the key bound, the causal diagonal or the bias band (or scale <= 0).
     // Per element the arithmetic is the fast path's (one FMA into exp2, with the
     // bias term folded into the addend), so the result of a row does not depend on
-    // which path a tile takes; masked keys get p = 0. The mask is evaluated again
-    // in phase 2 rather than kept in registers across the rescale.
+    // which path a tile takes; masked keys get p = 0. Band tiles and the other
+    // masked tiles take separate passes, so no per-element test of the tile's kind.
     // The bias of a band tile is read once, at the start of the tile step and
     // before that step's K/V prefetch goes out (waiting for these loads then does
     // not wait for the prefetch), into 16-bit pairs, with the mask folded in:
     // visible elements outside the band hold 0, masked ones the dtype's -inf.
     typedef uint32_t BiasBits[T::NQB][T::NKB][8];
+    // Visibility without per-element index arithmetic: key j = j0 + 32 kb2 + acc_row(r, hf)
+    // of row i is visible iff j < k_len and (causal) j <= i + delta, i.e. iff its
+    // offset 8 (r >> 2) + (r & 3) (the lane's 4 hf moved to the other side) is at most
+    // one per-lane limit per 32-key block; the offsets are immediates, so each test is
+    // one compare.
+    typedef int VisLim[T::NQB][T::NKB];
+    auto vis_limits = [&](VisLim& lim, int j0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) {
+            const int last = CAUSAL ? min(k_len - 1, qi[qb] + delta) : k_len - 1;  // last visible key
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++) lim[qb][kb2] = last - (j0 + kb2 * 32) - 4 * hf;
+        }
+    };
+    auto lim_vis = [](const VisLim& lim, int qb, int kb2, int r) __attribute__((always_inline)) {
+        return 8 * (r >> 2) + (r & 3) <= lim[qb][kb2];
+    };
     auto bias_row = [&](int qb) __attribute__((always_inline)) {
         return BIAS ? p.bias + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)p.E : nullptr;
     };
@@ -541,11 +558,15 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(((uint64_t)hi << 32) | lo), (short)0, nrec, 0x00020000);
+        VisLim lim;
+        vis_limits(lim, j0);
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
             const int i = qi[qb];
             const long long row = (q_off + i) * p.Hq + qh[qb];
             const int d0 = i + delta - j0 - 4 * hf;  // d of element (kb2, r) is d0 - c(kb2, r)
+            // in the band (0 <= d < E, valid row) iff blo <= c <= bhi
+            const int bhi = qvalid[qb] ? d0 : -1, blo = d0 - p.E + 1;
             const int vo = (int)((row - base_row) * p.E + d0 - CMAX) * 2;
             uint32_t raw[T::NKB][16];
 #pragma unroll
@@ -562,12 +583,12 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
                     uint32_t w = 0;
 #pragma unroll
                     for (int e = 0; e < 2; e++) {
-                        const int j = j0 + kb2 * 32 + acc_row(2 * r2 + e, hf);
-                        const int d = i + delta - j;
-                        const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
-                        const bool keep = vis && qvalid[qb] && d >= 0 && d < p.E;
+                        const int r = 2 * r2 + e;
+                        const int c = kb2 * 32 + 8 * (r >> 2) + (r & 3);
+                        const bool vis = lim_vis(lim, qb, kb2, r);
+                        const bool keep = vis && c <= bhi && c >= blo;
                         // masked: the -inf of the dtype; visible outside the band: 0
-                        const uint32_t h = (raw[kb2][2 * r2 + e] & (keep ? 0xFFFFu : 0u)) |
+                        const uint32_t h = (raw[kb2][r] & (keep ? 0xFFFFu : 0u)) |
                                            (vis ? 0u : (uint32_t)E::kNegInfBits);
                         w |= h << (16 * e);
                     }
@@ -641,6 +662,8 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         }
         // element (kb2, r) of the lane: u = BN - 1 - kb2 * 32 - acc_row(r, hf); a group of
         // four (r = 4g .. 4g + 3) is one aligned 8-byte read, its values in reverse order
+        VisLim lim;
+        vis_limits(lim, j0);
 #pragma unroll
         for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
@@ -655,8 +678,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
 #pragma unroll
                     for (int e = 0; e < 2; e++) {
                         const int r = 4 * g + 2 * h2 + e;
-                        const int j = j0 + kb2 * 32 + acc_row(r, hf);
-                        const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
+                        const bool vis = lim_vis(lim, 0, kb2, r);
                         const uint32_t v = (pr[h2] >> (16 * e)) & 0xFFFFu;
                         // masked: the -inf of the dtype; values outside [0, E) came out 0
                         w |= (vis ? v : (uint32_t)E::kNegInfBits) << (16 * e);
@@ -674,20 +696,11 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         else
             load_bias_from(bb, j0, [&](int qb) { return bias_row(qb); });
     };
-    auto slow_term = [&](int qb, int kb2, int r, int j0, bool band, const BiasBits& bb)
-        __attribute__((always_inline)) {
-        // a band tile's terms were formed with the mask folded in (masked keys hold
-        // -inf); other tiles work the mask out here
-        if (BIAS && band) return E::widen((uint16_t)(bb[qb][kb2][r >> 1] >> (16 * (r & 1)))) * kLog2e;
-        const int i = qi[qb];
-        const int j = j0 + kb2 * 32 + acc_row(r, hf);
-        const bool vis = (j < k_len) && (!CAUSAL || j <= i + delta);
-        return vis ? 0.f : -INFINITY;  // -inf marks a masked key
+    // A band tile's terms were formed with the mask folded in (masked keys hold -inf).
+    auto band_term = [&](int qb, int kb2, int r, const BiasBits& bb) __attribute__((always_inline)) {
+        return E::widen((uint16_t)(bb[qb][kb2][r >> 1] >> (16 * (r & 1)))) * kLog2e;
     };
-    auto max_slow = [&](STile& s, int j0, bool band, const BiasBits& bb) __attribute__((always_inline)) {
-        // opaque copy: keeps the per-element key indices inside the slow path
-        // instead of letting them be hoisted onto the fast path
-        asm volatile("" : "+s"(j0));
+    auto max_band = [&](STile& s, const BiasBits& bb) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
             float mx = -INFINITY;
@@ -695,14 +708,13 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const float b2 = slow_term(qb, kb2, r, j0, band, bb);
+                    const float b2 = band_term(qb, kb2, r, bb);
                     mx = fmaxf(mx, b2 == -INFINITY ? -INFINITY : __builtin_fmaf(s[qb][kb2][r], p.c2, b2));
                 }
             m_run[qb] = fmaxf(m_run[qb], partner_max(mx));
         }
     };
-    auto exp_slow = [&](STile& s, int j0, bool band, const BiasBits& bb) __attribute__((always_inline)) {
-        asm volatile("" : "+s"(j0));
+    auto exp_band = [&](STile& s, const BiasBits& bb) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
             const float mu = m_used[qb] == -INFINITY ? 0.f : m_used[qb];
@@ -711,9 +723,39 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const float b2 = slow_term(qb, kb2, r, j0, band, bb);
+                    const float b2 = band_term(qb, kb2, r, bb);
                     const float pv = b2 == -INFINITY ? 0.f
                                                      : __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, b2 - mu));
+                    s[qb][kb2][r] = pv;
+                    rs += pv;
+                }
+            l_run[qb] += rs;
+        }
+    };
+    // (a visible key's term is 0: the same FMA as the fast path, s * c2 - mu)
+    auto max_mask = [&](STile& s, const VisLim& lim) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++)
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    mx = fmaxf(mx, lim_vis(lim, qb, kb2, r) ? __builtin_fmaf(s[qb][kb2][r], p.c2, 0.f) : -INFINITY);
+            m_run[qb] = fmaxf(m_run[qb], partner_max(mx));
+        }
+    };
+    auto exp_mask = [&](STile& s, const VisLim& lim) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) {
+            const float mu = m_used[qb] == -INFINITY ? 0.f : m_used[qb];
+            float rs = 0.f;
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const float pv = lim_vis(lim, qb, kb2, r)
+                                         ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, -mu)) : 0.f;
                     s[qb][kb2][r] = pv;
                     rs += pv;
                 }
@@ -848,13 +890,19 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
             qk(kstage(st), s);
             // O is only touched in straight-line code (the rescale and PV), so the
             // fast / slow branches merge no accumulator state
+            // three kinds of tile, each pass chosen once per tile (uniform branches)
             const bool fast = !need_mask && !band && p.c2 > 0.f;
+            const bool banded = BIAS && band;
+            VisLim lim;
+            if (!fast && !banded) vis_limits(lim, j0);
             if (fast) max_fast(s);
-            else max_slow(s, j0, band, bb);
+            else if (banded) max_band(s, bb);
+            else max_mask(s, lim);
             update_used_max();
             rescale_acc();
             if (fast) exp_fast(s);
-            else exp_slow(s, j0, band, bb);
+            else if (banded) exp_band(s, bb);
+            else exp_mask(s, lim);
             lo_decision();
             pv(vstage(st), s);
         }
