@@ -24,7 +24,8 @@
 //     PREFETCH + 1 = 2 stages; the loads of the next tile are in flight while a
 //     tile is computed; one barrier per tile.
 //   * Only tiles that cross the key bound, the causal diagonal or the bias band
-//     run the per-element mask / bias code.
+//     run the per-element mask / bias code (band tiles and the other masked
+//     tiles in passes of their own).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -888,9 +889,10 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         if (D != 256 || (wave_live && (!CAUSAL || j0 <= wi_hi + delta))) {
             STile s;
             qk(kstage(st), s);
-            // O is only touched in straight-line code (the rescale and PV), so the
-            // fast / slow branches merge no accumulator state
-            // three kinds of tile, each pass chosen once per tile (uniform branches)
+            // Three kinds of tile (unmasked, band, other masked), each softmax pass
+            // chosen once per tile by a uniform branch. O is only touched in
+            // straight-line code (the rescale and PV), so the branches merge no
+            // accumulator state.
             const bool fast = !need_mask && !band && p.c2 > 0.f;
             const bool banded = BIAS && band;
             VisLim lim;
