@@ -774,12 +774,6 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         }
     };
 
-    // O^T += V^T P^T, 16 keys per MFMA step. bf16 P carries a 2^-9 relative
-    // rounding error; for a row whose normaliser is still small (few keys hold
-    // its weight) that error can reach the output tolerance, so such rows also
-    // feed the remainder P - bf16(P) through a second MFMA. A row with
-    // normaliser l (max weight 1) has at least l effective keys, and the error
-    // shrinks like 2^-9 / sqrt(3 l); rows at or above kLoThresh skip it.
     // which rows take the remainder MFMA for the tile whose exponentials were just added to l
     bool need_lo[T::NQB];
     bool any_lo = false;
