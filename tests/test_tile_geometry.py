@@ -97,3 +97,37 @@ def test_band_tile_bounds_edges():
     for args in [(1, 5000, 8, True, 128, 32), (300, 40, 1, True, 256, 64), (1, 1, 1, False, 128, 64),
                  (129, 129, 1, True, 128, 64), (64, 2000, 8, False, 384, 64)]:
         check_shape(*args)
+
+
+def test_visibility_limit_and_band_bounds():
+    """The kernel tests a key's visibility as one compare of its in-tile offset
+    8 (r >> 2) + (r & 3) against a per-lane limit
+        lim = (causal ? min(k_len - 1, i + delta) : k_len - 1) - (j0 + 32 kb2) - 4 hf,
+    and a band element (0 <= d < E, valid row) as blo <= c <= bhi with
+        c = 32 kb2 + 8 (r >> 2) + (r & 3), d0 = i + delta - j0 - 4 hf,
+        bhi = valid ? d0 : -1, blo = d0 - E + 1.
+    Both must agree with the direct definitions for every element of every tile."""
+    rng = gen.make_rng(5151)
+    for _ in range(400):
+        q_len = int(rng.integers(1, 300))
+        k_len = int(rng.integers(0, 400))
+        causal = bool(rng.random() < 0.5)
+        E = int(rng.choice([128, 256]))
+        nkb = int(rng.choice([1, 2, 4]))
+        delta = k_len - q_len
+        i = int(rng.integers(0, q_len))
+        valid = bool(rng.random() < 0.9)
+        j0 = 32 * nkb * int(rng.integers(0, max(1, (k_len + 32 * nkb - 1) // (32 * nkb)) + 1))
+        for hf in range(2):
+            last = min(k_len - 1, i + delta) if causal else k_len - 1
+            d0 = i + delta - j0 - 4 * hf
+            bhi, blo = (d0 if valid else -1), d0 - E + 1
+            for kb2 in range(nkb):
+                lim = last - (j0 + 32 * kb2) - 4 * hf
+                for r in range(16):
+                    j = j0 + 32 * kb2 + acc_row(r, hf)
+                    vis = j < k_len and (not causal or j <= i + delta)
+                    assert (8 * (r >> 2) + (r & 3) <= lim) == vis
+                    c = 32 * kb2 + 8 * (r >> 2) + (r & 3)
+                    d = i + delta - j
+                    assert (blo <= c <= bhi) == (valid and 0 <= d < E)
