@@ -17,7 +17,7 @@ from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 96
+N_CASES = 296
 
 
 @pytest.fixture(scope="module", autouse=True)
