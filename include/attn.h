@@ -169,7 +169,8 @@ attn_status_t attn_check_args(const void* q, const void* k, const void* v, void*
  * x 1 for D = 256); then use n = floor(that / work-groups) splits (one wave of
  * work-groups fills the chip), times r = min(8, floor(key blocks / n / 64)) when
  * r > 1 (several waves while each split keeps at least 64 key blocks), never
- * fewer than 4 key blocks per split (64 keys per block; 128 for D <= 16).
+ * fewer than 4 key blocks per split (64 keys per block; 128 for D <= 16) and
+ * never more than ATTN_MAX_SPLITS splits.
  */
 int attn_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_varlen,
                     int max_seqlen_q, int max_seqlen_k, int pack_gqa, int num_splits);
