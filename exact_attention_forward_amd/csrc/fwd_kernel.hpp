@@ -719,8 +719,8 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const float b2 = band_term(qb, kb2, r, bb);
-                    mx = fmaxf(mx, b2 == -INFINITY ? -INFINITY : __builtin_fmaf(s[qb][kb2][r], p.c2, b2));
+                    // a masked key's term is -inf, and so is the FMA (scores are finite)
+                    mx = fmaxf(mx, __builtin_fmaf(s[qb][kb2][r], p.c2, band_term(qb, kb2, r, bb)));
                 }
             m_run[qb] = fmaxf(m_run[qb], partner_max(mx));
         }
@@ -734,9 +734,8 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const float b2 = band_term(qb, kb2, r, bb);
-                    const float pv = b2 == -INFINITY ? 0.f
-                                                     : __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, b2 - mu));
+                    // exp2(-inf) = 0 for a masked key
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, band_term(qb, kb2, r, bb) - mu));
                     s[qb][kb2][r] = pv;
                     rs += pv;
                 }
