@@ -341,7 +341,7 @@ def main():
     # preallocate everything: the timed calls allocate nothing
     out, lse = fa.attn_fwd(q, k, v, **kw)
     ns = fa.num_splits(spec.B, spec.Sq, spec.Sk, spec.Hq, spec.Hkv, spec.D, spec.Dv,
-                       is_varlen=varlen, max_seqlen_q=x.get("max_seqlen_q", 0),
+                       causal=spec.causal, is_varlen=varlen, max_seqlen_q=x.get("max_seqlen_q", 0),
                        max_seqlen_k=x.get("max_seqlen_k", 0), pack_gqa=spec.pack_gqa,
                        requested=spec.num_splits)
     ws = None

@@ -44,7 +44,7 @@ SIGNATURES = {
                                _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]),
     "attn_check_args": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _I,
                              _P, _P, _I, _I, _I, _I, _P, _Z]),
-    "attn_num_splits": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "attn_num_splits": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "attn_fwd_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
     "attn_combine": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
@@ -113,15 +113,67 @@ def _stream_handle(stream, device):
     return stream.cuda_stream
 
 
-def num_splits(B, Sq, Sk, Hq, Hkv, D, Dv, *, is_varlen=False, max_seqlen_q=0, max_seqlen_k=0,
-               pack_gqa=-1, requested=0) -> int:
+def num_splits(B, Sq, Sk, Hq, Hkv, D, Dv, *, causal=False, is_varlen=False, max_seqlen_q=0,
+               max_seqlen_k=0, pack_gqa=-1, requested=0) -> int:
     """Split count attn_fwd uses (requested <= 0: the heuristic)."""
-    return load().attn_num_splits(B, Sq, Sk, Hq, Hkv, D, Dv, int(bool(is_varlen)), max_seqlen_q,
-                                  max_seqlen_k, pack_gqa, requested)
+    return load().attn_num_splits(B, Sq, Sk, Hq, Hkv, D, Dv, int(bool(causal)), int(bool(is_varlen)),
+                                  max_seqlen_q, max_seqlen_k, pack_gqa, requested)
 
 
 def workspace_size(B, Sq, Hq, Dv, *, is_varlen=False, splits=1) -> int:
     return load().attn_fwd_workspace_size(B, Sq, Hq, Dv, int(bool(is_varlen)), splits)
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensors(q, k, v, *, varlen, B, Sq, Hq, D, cu_seqlens_q, cu_seqlens_k, seqused_k, rel_bias,
+                   rel_r, rel_proj, out, lse, workspace, out_shape, lse_shape):
+    """Shape, dtype, layout and device checks done before any pointer reaches the library
+    (the C entry points see only pointers and sizes, so a wrong tensor would be read or
+    written out of bounds)."""
+    import torch
+    nd = 3 if varlen else 4
+    _require(k.dim() == nd and v.dim() == nd, f"k and v must have q's rank ({nd})")
+    if varlen:
+        _require(k.shape[2] == D, f"k {tuple(k.shape)} must be [total_k, Hkv, D={D}]")
+        _require(v.shape[:2] == k.shape[:2], f"v {tuple(v.shape)} must be [total_k, Hkv, Dv] like k")
+    else:
+        _require(k.shape[0] == B and k.shape[3] == D, f"k {tuple(k.shape)} must be [B={B}, Sk, Hkv, D={D}]")
+        _require(v.shape[:3] == k.shape[:3], f"v {tuple(v.shape)} must be [B, Sk, Hkv, Dv] like k")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t is not None:
+            _require(t.dtype == torch.int32 and t.dim() == 1 and t.numel() == B + 1 and t.is_contiguous(),
+                     f"{name} must be a contiguous int32 tensor of B + 1 = {B + 1} elements")
+    if seqused_k is not None:
+        _require(seqused_k.dtype == torch.int32 and seqused_k.dim() == 1 and seqused_k.numel() == B and
+                 seqused_k.is_contiguous(), f"seqused_k must be a contiguous int32 tensor of B = {B} elements")
+    rows_q = Sq if varlen else B * Sq
+    if rel_bias is not None:
+        _require(rel_bias.dim() == 3 and rel_bias.shape[0] == rows_q and rel_bias.shape[1] == Hq,
+                 f"rel_bias {tuple(rel_bias.shape)} must be [rows_q={rows_q}, Hq={Hq}, rel_extent]")
+    if rel_r is not None:
+        _require(rel_r.dim() == 3 and rel_r.shape[0] == rows_q and rel_r.shape[1] == Hq,
+                 f"rel_r {tuple(rel_r.shape)} must be [rows_q={rows_q}, Hq={Hq}, d_rel]")
+        _require(rel_proj.dim() == 2 and rel_proj.shape[0] == rel_r.shape[2],
+                 f"rel_proj {tuple(rel_proj.shape)} must be [d_rel={rel_r.shape[2]}, rel_extent]")
+    if out is not None:
+        _require(tuple(out.shape) == tuple(out_shape) and out.dtype == q.dtype and out.is_contiguous(),
+                 f"out must be a contiguous {q.dtype} tensor of shape {tuple(out_shape)}")
+    if lse is not None:
+        _require(tuple(lse.shape) == tuple(lse_shape) and lse.dtype == torch.float32 and lse.is_contiguous(),
+                 f"lse must be a contiguous float32 tensor of shape {tuple(lse_shape)}")
+    if workspace is not None:
+        _require(workspace.is_contiguous(), "workspace must be contiguous")
+    dev = q.device
+    _require(dev.type == "cuda", "q must be a CUDA (ROCm) tensor: the forward runs only on the GPU")
+    for name, t in (("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
+                    ("seqused_k", seqused_k), ("rel_bias", rel_bias), ("rel_r", rel_r), ("rel_proj", rel_proj),
+                    ("out", out), ("lse", lse), ("workspace", workspace)):
+        if t is not None:
+            _require(t.device == dev, f"{name} must be on {dev} like q (it is on {t.device})")
 
 
 def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
@@ -144,6 +196,7 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
     if varlen:
         if q.dim() != 3:
             raise ValueError("varlen q must be [total_q, Hq, D]")
+        _require(k.dim() == 3 and v.dim() == 3, "varlen k and v must be [total_k, Hkv, D] and [total_k, Hkv, Dv]")
         Sq, Hq, D = q.shape
         Sk, Hkv, _ = k.shape
         Dv = v.shape[-1]
@@ -155,6 +208,7 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
     else:
         if q.dim() != 4:
             raise ValueError("dense q must be [B, Sq, Hq, D]")
+        _require(k.dim() == 4 and v.dim() == 4, "dense k and v must be [B, Sk, Hkv, D] and [B, Sk, Hkv, Dv]")
         B, Sq, Hq, D = q.shape
         _, Sk, Hkv, _ = k.shape
         Dv = v.shape[-1]
@@ -170,21 +224,25 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
     dtype = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty(out_shape, dtype=q.dtype, device=q.device)
-    if lse is None and return_lse:
-        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
     if rel_r is not None or rel_proj is not None:
         if rel_bias is not None or rel_r is None or rel_proj is None:
             raise ValueError("pass rel_r with rel_proj, or rel_bias, not both")
         for name, t in (("rel_r", rel_r), ("rel_proj", rel_proj)):
             if not t.is_contiguous() or t.dtype != q.dtype:
                 raise ValueError(f"{name} must be contiguous and of q's dtype")
+    _check_tensors(q, k, v, varlen=varlen, B=B, Sq=Sq, Hq=Hq, D=D, cu_seqlens_q=cu_seqlens_q,
+                   cu_seqlens_k=cu_seqlens_k, seqused_k=seqused_k, rel_bias=rel_bias, rel_r=rel_r,
+                   rel_proj=rel_proj, out=out, lse=lse, workspace=workspace, out_shape=out_shape,
+                   lse_shape=lse_shape)
+    if out is None:
+        out = torch.empty(out_shape, dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
     E = 0 if rel_bias is None else int(rel_bias.shape[-1])
     if rel_proj is not None:
         E = int(rel_proj.shape[1])
-    ns = lib.attn_num_splits(B, Sq, Sk, Hq, Hkv, D, Dv, int(varlen), max_seqlen_q, max_seqlen_k,
-                             pack_gqa, num_splits)
+    ns = lib.attn_num_splits(B, Sq, Sk, Hq, Hkv, D, Dv, int(bool(causal)), int(varlen), max_seqlen_q,
+                             max_seqlen_k, pack_gqa, num_splits)
     ws_bytes = 0
     if ns > 1:
         ws_bytes = lib.attn_fwd_workspace_size(B, Sq, Hq, Dv, int(varlen), ns)
@@ -210,12 +268,47 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
 
 def attn_combine(o_partial, lse_partial, *, out, lse=None, B: int, Sq: int, is_varlen: bool = False,
                  stream=None):
-    """LSE-weighted merge of split partials (fp32) into out (bf16/fp16) and lse (fp32)."""
+    """LSE-weighted merge of split partials (fp32) into out (bf16/fp16) and lse (fp32).
+
+    Dense: o_partial [ns, B*Sq, Hq, Dv], lse_partial [ns, B, Hq, Sq], out [B, Sq, Hq, Dv], lse [B, Hq, Sq].
+    Varlen (Sq = total_q): o_partial [ns, Sq, Hq, Dv], lse_partial [ns, Hq, Sq], out [Sq, Hq, Dv],
+    lse [Hq, Sq]. These are the layouts attn_fwd leaves in its workspace.
+    """
+    import torch
     lib = load()
-    ns = o_partial.shape[0]
-    Hq = o_partial.shape[-2]
-    Dv = o_partial.shape[-1]
+    _require(o_partial.dim() == 4, "o_partial must be [num_splits, rows_q, Hq, Dv]")
+    ns, rows_q, Hq, Dv = (int(x) for x in o_partial.shape)
+    _require(rows_q == (Sq if is_varlen else B * Sq), f"o_partial has {rows_q} rows, expected "
+             f"{Sq if is_varlen else B * Sq}")
+    lse_p_shape = (ns, Hq, Sq) if is_varlen else (ns, B, Hq, Sq)
+    out_shape = (Sq, Hq, Dv) if is_varlen else (B, Sq, Hq, Dv)
+    lse_shape = lse_p_shape[1:]
+    _require(o_partial.dtype == torch.float32 and o_partial.is_contiguous(), "o_partial must be contiguous float32")
+    _require(tuple(lse_partial.shape) == lse_p_shape and lse_partial.dtype == torch.float32 and
+             lse_partial.is_contiguous(), f"lse_partial must be a contiguous float32 tensor of shape {lse_p_shape}")
+    _require(tuple(out.shape) == out_shape and out.is_contiguous(), f"out must be contiguous, shape {out_shape}")
+    if lse is not None:
+        _require(tuple(lse.shape) == lse_shape and lse.dtype == torch.float32 and lse.is_contiguous(),
+                 f"lse must be a contiguous float32 tensor of shape {lse_shape}")
+    dev = out.device
+    _require(dev.type == "cuda", "out must be a CUDA (ROCm) tensor: the combine runs only on the GPU")
+    for name, t in (("o_partial", o_partial), ("lse_partial", lse_partial), ("lse", lse)):
+        if t is not None:
+            _require(t.device == dev, f"{name} must be on {dev} like out (it is on {t.device})")
     st = lib.attn_combine(_ptr(o_partial), _ptr(lse_partial), ns, _ptr(out), _ptr(lse), B, Sq, Hq, Dv,
                           int(bool(is_varlen)), _dtype_code(out), _stream_handle(stream, out.device))
     _check(st)
     return out, lse
+
+
+def split_partials(workspace, num_splits: int, *, B: int, Sq: int, Hq: int, Dv: int, is_varlen: bool = False):
+    """Views of attn_fwd's workspace as (o_partial, lse_partial) for attn_combine: fp32 O
+    [num_splits, rows_q, Hq, Dv] followed by fp32 LSE [num_splits, <lse layout>]."""
+    import torch
+    rows_q = Sq if is_varlen else B * Sq
+    n_o = num_splits * rows_q * Hq * Dv
+    n_l = num_splits * rows_q * Hq
+    flat = workspace.view(torch.uint8)[: (n_o + n_l) * 4].view(torch.float32)
+    o_p = flat[:n_o].view(num_splits, rows_q, Hq, Dv)
+    l_p = flat[n_o:].view((num_splits, Hq, Sq) if is_varlen else (num_splits, B, Hq, Sq))
+    return o_p, l_p

@@ -11,6 +11,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "../../include/attn.h"
 #include "kernels.h"
 
@@ -18,7 +20,28 @@ using namespace mi355attn;
 
 namespace {
 
-constexpr int kNumCUs = 256;  // MI355X compute units
+constexpr int kFullChipCUs = 256;  // MI355X compute units (all XCDs of one GPU)
+
+// Compute units of the current device, queried once per device (a partitioned MI355X
+// shows fewer); the full chip's count when no device is visible, so the host-only
+// entry points keep working without a GPU.
+int num_cus() {
+    static std::atomic<int> cached[64];
+    static std::atomic<int> no_device{0};
+    if (no_device.load(std::memory_order_relaxed)) return kFullChipCUs;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        no_device.store(1, std::memory_order_relaxed);
+        return kFullChipCUs;
+    }
+    if (dev >= 64) return kFullChipCUs;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = kFullChipCUs;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 bool is_aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -39,7 +62,7 @@ bool mul_ok(long long& acc, long long x) {
 }
 
 struct Plan {
-    bool varlen;
+    bool varlen, causal;
     int G, gp, n_hg, n_tiles, ns, nkb_max;
     int dclass;  // head-dim class the kernel is compiled for
     bool dsplit; // class 256 with at most 32 rows per tile: the waves share out the V columns
@@ -48,7 +71,7 @@ struct Plan {
 };
 
 // Tile geometry shared with the kernels; returns false for sizes that cannot be planned.
-bool make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_varlen, int max_seqlen_q,
+bool make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int causal, int is_varlen, int max_seqlen_q,
                int max_seqlen_k, int pack_gqa, int num_splits, Plan& pl) {
     if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || !head_dim_ok(D) ||
         !head_dim_ok(Dv))
@@ -56,13 +79,15 @@ bool make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_var
     pl.dclass = head_dim_class(D > Dv ? D : Dv);
     const int dc = pl.dclass;
     pl.varlen = is_varlen != 0;
+    pl.causal = causal != 0;
     pl.G = Hq / Hkv;
     const bool pack = pack_gqa == 1 || (pack_gqa == -1 && pl.G > 1);
     pl.gp = pack ? pl.G : 1;
     pl.n_hg = pack ? Hkv : Hq;
     const long long qmax = pl.varlen ? max_seqlen_q : Sq;
     const long long kmax = pl.varlen ? max_seqlen_k : Sk;
-    const int bm = tile_bm(dc), bn = tile_bn(dc);
+    const int bm = tile_bm(dc, pl.causal), bn = tile_bn(dc);
+    const long long resident = (long long)num_cus() * tile_wg_per_cu(dc, pl.causal);
     const long long nt = (qmax * pl.gp + bm - 1) / bm;
     if (nt > INT32_MAX) return false;
     pl.n_tiles = (int)nt;
@@ -77,13 +102,13 @@ bool make_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_var
         ns = num_splits;
         if (ns > pl.nkb_max) ns = pl.nkb_max;
         if (ns > ATTN_MAX_SPLITS) ns = ATTN_MAX_SPLITS;
-    } else if (base == 0 || base >= (long long)kNumCUs * tile_wg_per_cu(dc)) {
+    } else if (base == 0 || base >= resident) {
         ns = 1;
     } else {
         // one wave of resident work-groups: CUs x work-groups per CU; then up to 8 such
         // waves while each split keeps at least 64 key blocks (the tail of the last
         // wave weighs less; measured c4c -12%, n1c -5% time against one wave)
-        ns = (int)((long long)kNumCUs * tile_wg_per_cu(dc) / base);
+        ns = (int)(resident / base);
         if (ns >= 1) {
             long long rounds = (long long)pl.nkb_max / ns / 64;
             if (rounds > 8) rounds = 8;
@@ -105,7 +130,7 @@ size_t workspace_bytes_for(long long rows_q, int Hq, int Dv, int ns) {
 }
 
 attn_status_t validate(const void* q, const void* k, const void* v, void* out, float* lse, int B,
-                       int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale,
+                       int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale, int causal,
                        const int* cu_q, const int* cu_k, int max_seqlen_q, int max_seqlen_k,
                        const void* rel_bias, int rel_extent, int num_splits, int pack_gqa,
                        attn_dtype_t dtype, void* workspace, size_t workspace_bytes, Plan& pl) {
@@ -113,8 +138,15 @@ attn_status_t validate(const void* q, const void* k, const void* v, void* out, f
     if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Dv <= 0) return ATTN_ERR_BAD_SHAPE;
     if (!head_dim_ok(D) || !head_dim_ok(Dv)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
     if (Hq % Hkv) return ATTN_ERR_BAD_GQA;
-    // a K/V tile (64 keys) must span fewer than 2^31 bytes: buffer offsets are 32-bit
-    if ((long long)Hkv * (D > Dv ? D : Dv) > (1LL << 23)) return ATTN_ERR_BAD_SHAPE;
+    // The bytes of one K or V tile (tile_bn keys, consecutive keys Hkv * head dim * 2 bytes
+    // apart) must not exceed 2^30: the kernels give the columns past D (Dv) a fixed load
+    // offset of 2^30, which has to fall outside every tile's buffer range (and the range
+    // is a 32-bit count). Hkv * max(D, Dv) <= 2^23, or 2^22 at head-dim class 16 (128-key
+    // tiles).
+    {
+        const int dmax = D > Dv ? D : Dv;
+        if ((long long)tile_bn(head_dim_class(dmax)) * Hkv * dmax * 2 > (1LL << 30)) return ATTN_ERR_BAD_SHAPE;
+    }
     if (!isfinite(scale)) return ATTN_ERR_BAD_SCALE;
     if (pack_gqa < -1 || pack_gqa > 1) return ATTN_ERR_BAD_ARG;
     if ((cu_q == nullptr) != (cu_k == nullptr)) return ATTN_ERR_BAD_VARLEN;
@@ -142,7 +174,7 @@ attn_status_t validate(const void* q, const void* k, const void* v, void* out, f
     } else if (rel_extent != 0) {
         return ATTN_ERR_BAD_REL_EXTENT;
     }
-    if (!make_plan(B, Sq, Sk, Hq, Hkv, D, Dv, varlen, max_seqlen_q, max_seqlen_k, pack_gqa, num_splits, pl))
+    if (!make_plan(B, Sq, Sk, Hq, Hkv, D, Dv, causal, varlen, max_seqlen_q, max_seqlen_k, pack_gqa, num_splits, pl))
         return ATTN_ERR_BAD_SHAPE;
     if (pl.nblocks > INT32_MAX) return ATTN_ERR_BAD_SHAPE;
     const bool has_rows = pl.rows_q > 0 && B > 0;
@@ -176,18 +208,17 @@ attn_status_t attn_check_args(const void* q, const void* k, const void* v, void*
                               int max_seqlen_q, int max_seqlen_k, const int* seqused_k,
                               const void* rel_bias, int rel_extent, int num_splits, int pack_gqa,
                               attn_dtype_t dtype, void* workspace, size_t workspace_bytes) {
-    (void)causal;
     (void)seqused_k;
     Plan pl;
-    return validate(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, Dv, scale, cu_seqlens_q, cu_seqlens_k,
+    return validate(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, Dv, scale, causal, cu_seqlens_q, cu_seqlens_k,
                     max_seqlen_q, max_seqlen_k, rel_bias, rel_extent, num_splits, pack_gqa, dtype,
                     workspace, workspace_bytes, pl);
 }
 
-int attn_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_varlen,
+int attn_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int causal, int is_varlen,
                     int max_seqlen_q, int max_seqlen_k, int pack_gqa, int num_splits) {
     Plan pl;
-    if (!make_plan(B, Sq, Sk, Hq, Hkv, D, Dv, is_varlen, max_seqlen_q, max_seqlen_k, pack_gqa, num_splits, pl))
+    if (!make_plan(B, Sq, Sk, Hq, Hkv, D, Dv, causal, is_varlen, max_seqlen_q, max_seqlen_k, pack_gqa, num_splits, pl))
         return 0;
     return pl.ns;
 }
@@ -202,8 +233,8 @@ namespace {
 
 // LDS the fused producer needs past the K/V ring: one key tile's bias values for each
 // of the work-group's BM rows (BM x BN x 2 bytes, whatever rel_extent is)
-long long rel_rows_lds_bytes(int dclass) {
-    return (long long)tile_bm(dclass) * tile_bn(dclass) * 2;
+long long rel_rows_lds_bytes(int dclass, bool causal) {
+    return (long long)tile_bm(dclass, causal) * tile_bn(dclass) * 2;
 }
 
 // The fused-producer arguments on top of validate(): r and rel_proj given, d_rel a
@@ -212,7 +243,8 @@ attn_status_t validate_rel_proj(const void* rel_r, const void* rel_proj, int d_r
     if (!rel_r || !rel_proj) return ATTN_ERR_NULL_POINTER;
     if (d_rel < 8 || d_rel > 256 || d_rel % 8) return ATTN_ERR_BAD_ARG;
     if (!is_aligned(rel_r, 16) || !is_aligned(rel_proj, 2)) return ATTN_ERR_MISALIGNED;
-    if (tile_ring_bytes(pl.dclass) + rel_rows_lds_bytes(pl.dclass) > kLdsBytesPerCU / tile_wg_per_cu(pl.dclass))
+    if (tile_ring_bytes(pl.dclass) + rel_rows_lds_bytes(pl.dclass, pl.causal) >
+        kLdsBytesPerCU / tile_wg_per_cu(pl.dclass, pl.causal))
         return ATTN_ERR_UNSUPPORTED_COMBO;  // (never: the ring and this region fit beside each other)
     return ATTN_OK;
 }
@@ -233,7 +265,7 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, f
                        size_t workspace_bytes, void* stream) {
     Plan pl;
     const attn_status_t st =
-        validate(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, Dv, scale, cu_seqlens_q, cu_seqlens_k,
+        validate(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, Dv, scale, causal, cu_seqlens_q, cu_seqlens_k,
                  max_seqlen_q, max_seqlen_k, rel_bias, rel_extent, num_splits, pack_gqa, dtype,
                  workspace, workspace_bytes, pl);
     if (st != ATTN_OK) return st;
@@ -254,7 +286,7 @@ attn_status_t attn_fwd_rel_proj(const void* q, const void* k, const void* v, voi
     // validate as a call with a bias tensor (r stands in for its pointer: same row
     // order and dtype), then the producer's own arguments
     attn_status_t st =
-        validate(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, Dv, scale, cu_seqlens_q, cu_seqlens_k,
+        validate(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, Dv, scale, causal, cu_seqlens_q, cu_seqlens_k,
                  max_seqlen_q, max_seqlen_k, rel_r ? rel_r : rel_proj, rel_extent, num_splits, pack_gqa,
                  dtype, workspace, workspace_bytes, pl);
     if (st != ATTN_OK) return st;
@@ -285,7 +317,7 @@ attn_status_t run_fwd(const Plan& pl, const void* q, const void* k, const void* 
     p.rel_r = (const uint16_t*)rel_r;
     p.rel_proj = (const uint16_t*)rel_proj;
     p.d_rel = d_rel;
-    p.lds_extra = rel_r ? (int)rel_rows_lds_bytes(pl.dclass) : 0;
+    p.lds_extra = rel_r ? (int)rel_rows_lds_bytes(pl.dclass, pl.causal) : 0;
     p.o_part = nullptr;
     p.lse_part = nullptr;
     if (pl.ns > 1) {
@@ -397,6 +429,6 @@ const char* attn_status_string(attn_status_t s) {
     return "unknown status";
 }
 
-const char* attn_version(void) { return "mi355-attn 0.1.0 gfx950"; }
+const char* attn_version(void) { return "mi355-attn 0.2.0 gfx950"; }
 
 }  // extern "C"

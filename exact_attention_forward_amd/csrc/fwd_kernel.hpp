@@ -31,6 +31,7 @@
 #include <stdint.h>
 
 #include <array>
+#include <atomic>
 #include <utility>
 
 #include "kernels.h"
@@ -89,12 +90,12 @@ struct Elem<false> {  // IEEE half
     static constexpr uint16_t kNegInfBits = 0xFC00;
 };
 
-template <int D>
+template <int D, bool CAUSAL = false>
 struct Tile {
-    static constexpr int NW = 4;                  // waves per work-group
+    static constexpr int NW = tile_nw(D, CAUSAL); // waves per work-group
     static constexpr int NT = NW * 64;            // threads
     static constexpr int NQB = tile_nqb(D);       // 32-row blocks per wave
-    static constexpr int BM = tile_bm(D);         // rows per work-group
+    static constexpr int BM = tile_bm(D, CAUSAL); // rows per work-group
     static constexpr int BN = tile_bn(D);         // keys per tile
     static constexpr int NC = D / 16;             // 16-wide steps of the QK contraction
     static constexpr int NDT = (D + 31) / 32;     // 32-wide dv blocks of O^T
@@ -104,7 +105,7 @@ struct Tile {
     static constexpr int TILE_BYTES = BN * D * 2; // one K or V tile in LDS
     static constexpr int PREFETCH = tile_prefetch(D);  // tiles loaded ahead of the one being consumed
     static constexpr int NB = PREFETCH + 1;       // LDS ring stages, each a K tile and a V tile
-    static constexpr int WG_PER_CU = tile_wg_per_cu(D);
+    static constexpr int WG_PER_CU = tile_wg_per_cu(D, CAUSAL);
     // load offsets and K read addresses formed per tile instead of held in registers
     // across the key loop: fewer live registers for a few more VALU operations
     // (measured: faster at head-dim classes 16 and 256, slower at 64 and 128)
@@ -165,9 +166,9 @@ __device__ __forceinline__ void wait_vm_all() { wait_vm_loads<0>(); }
 // and accumulates a quarter of the V columns, so the PV MFMAs of a tile are shared
 // out instead of all falling to the one wave that holds rows.
 template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT, bool DSPLIT>
-__global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const FwdParams p) {
-    using T = Tile<D>;
-    static_assert(!DSPLIT || (D == 256 && T::NQB == 1), "dv split: class 256, one row block");
+__global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PER_CU)) attn_fwd_kernel(const FwdParams p) {
+    using T = Tile<D, CAUSAL>;
+    static_assert(!DSPLIT || (D == 256 && T::NQB == 1 && T::NW == 4), "dv split: class 256, one row block, four waves");
     constexpr int ODT = DSPLIT ? T::NDT / 4 : T::NDT;  // dv blocks of O^T this wave accumulates
     using E = Elem<BF>;
     typedef typename E::v8 v8;
@@ -450,7 +451,7 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
                 for (int dt = 0; dt < ODT; dt++) {
                     f32x16 x = o[qb][dt];
                     x *= alpha[qb];
-                    if (T::WG_PER_CU == 1) asm volatile("" : "+a"(x));  // one block at a time
+                    if (D == 256) asm volatile("" : "+a"(x));  // (512 registers a wave) one block at a time
                     o[qb][dt] = x;
                 }
         }
@@ -477,16 +478,11 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
             const float mu = m_used[qb];
-            float rs = 0.f;
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, -mu));
-                    s[qb][kb2][r] = pv;
-                    rs += pv;
-                }
-            l_run[qb] += rs;
+                for (int r = 0; r < 16; r++)
+                    s[qb][kb2][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, -mu));
         }
     };
 
@@ -612,91 +608,96 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
     bias_first_row = (long long)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)bias_first_row >> 32)) << 32) |
                                  __builtin_amdgcn_readfirstlane((uint32_t)bias_first_row));
     // Fused producer (tml-fa4 page: rel_bias = r . rel_proj, the einsum over d_rel), per
-    // band tile and wave. Over the wave's rows the tile needs d in [dbase, dbase + BN + 31)
-    // with dbase = wi_lo + delta - j0 - (BN - 1); the MFMA forms C[d][row] = rel_proj^T r^T
+    // band tile, wave and 32-row block. Over the block's rows the tile needs d in
+    // [dbase, dbase + BN + 31) with dbase = (block's first query) + delta - j0 - (BN - 1);
+    // the MFMA forms C[d][row] = rel_proj^T r^T
     // for that range in 32-d blocks (A = a rel_proj column per lane, zero outside [0, E);
     // B = the lane's r row), so each lane ends up holding values of its own row. Rounded
     // to the dtype (as a materialised rel_bias is), they go to the row's LDS slot of BN
-    // values, slot u holding d = dbase + (row - wi_lo) + u: the first and the last block
+    // values, slot u holding d = dbase + (query - first query) + u: the first and the last block
     // share the slots (u = (m - off) mod BN takes the first block's value for m >= off,
     // the last one's below), the blocks between fill theirs whole, so every write is
     // unconditional. The tile's elements then read their d at a fixed u per element.
     auto produce_bias = [&](BiasBits& bb, int j0) __attribute__((always_inline)) {
-        static_assert(T::NQB == 1, "one 32-row block per wave");
         constexpr int NBLK = T::NKB + 1;  // 32-d blocks covering BN + 31 values
-        const int dbase = wi_lo + delta - j0 - (T::BN - 1);
-        const int i = qi[0];
-        const int off = i - wi_lo;  // 0 .. 31
-        uint16_t* slot = bias_lds + (wave * 32 + l32) * T::BN;
         // opaque copies: the addresses below are formed per tile instead of being
         // hoisted out of the key loop into registers held across it
         int E_ = p.E, drel = p.d_rel;
         asm volatile("" : "+s"(E_), "+s"(drel));
-        const uint16_t* rrow = p.rel_r + ((q_off + i) * p.Hq + qh[0]) * (long long)drel;
         const uint16_t* proj = p.rel_proj;
-        auto block = [&](int b) __attribute__((always_inline)) {
-            f32x16 c = {};
-            const int dcol = dbase + 32 * b + l32;  // the A row (d) this lane provides
-            const bool din = dcol >= 0 && dcol < E_;
-            const uint16_t* pcol = proj + min(max(dcol, 0), E_ - 1);
-            for (int k0 = 0; k0 < drel; k0 += 16) {
-                const int ka = k0 + 8 * hf;  // this lane's 8 contraction indices
-                u32x4 bw = {0u, 0u, 0u, 0u};
-                if (ka < drel) bw = *(const u32x4*)(rrow + ka);
-                u32x4 aw = {0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const int k1 = min(ka + e, drel - 1), k2 = min(ka + e + 1, drel - 1);
-                    const uint32_t v1 = pcol[k1 * E_];
-                    const uint32_t v2 = pcol[k2 * E_];
-                    const uint32_t keep1 = din && ka + e < drel ? 0xFFFFu : 0u;
-                    const uint32_t keep2 = din && ka + e + 1 < drel ? 0xFFFFu : 0u;
-                    aw[e >> 1] = (v1 & keep1) | ((v2 & keep2) << 16);
-                }
-                c = E::mma(__builtin_bit_cast(v8, aw), __builtin_bit_cast(v8, bw), c);
-            }
-            return c;
-        };
-        {
-            const f32x16 cf = block(0), cl = block(NBLK - 1);
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = acc_row(r, hf);
-                slot[(m - off) & (T::BN - 1)] = E::narrow(m >= off ? cf[r] : cl[r]);
-            }
-        }
-#pragma unroll
-        for (int b = 1; b < NBLK - 1; b++) {
-            const f32x16 c = block(b);
-#pragma unroll
-            for (int r = 0; r < 16; r++) slot[32 * b + acc_row(r, hf) - off] = E::narrow(c[r]);
-        }
-        // element (kb2, r) of the lane: u = BN - 1 - kb2 * 32 - acc_row(r, hf); a group of
-        // four (r = 4g .. 4g + 3) is one aligned 8-byte read, its values in reverse order
         VisLim lim;
         vis_limits(lim, j0);
 #pragma unroll
-        for (int kb2 = 0; kb2 < T::NKB; kb2++)
+        for (int qb = 0; qb < T::NQB; qb++) {
+            // this row block's first query (rows past the last one repeat it)
+            const int blo = min(w_row + 32 * qb, r_last) / gp;
+            const int dbase = blo + delta - j0 - (T::BN - 1);
+            const int i = qi[qb];
+            const int off = i - blo;  // 0 .. 31
+            uint16_t* slot = bias_lds + ((wave * T::NQB + qb) * 32 + l32) * T::BN;
+            const uint16_t* rrow = p.rel_r + ((q_off + i) * p.Hq + qh[qb]) * (long long)drel;
+            auto block = [&](int b) __attribute__((always_inline)) {
+                f32x16 c = {};
+                const int dcol = dbase + 32 * b + l32;  // the A row (d) this lane provides
+                const bool din = dcol >= 0 && dcol < E_;
+                const uint16_t* pcol = proj + min(max(dcol, 0), E_ - 1);
+                for (int k0 = 0; k0 < drel; k0 += 16) {
+                    const int ka = k0 + 8 * hf;  // this lane's 8 contraction indices
+                    u32x4 bw = {0u, 0u, 0u, 0u};
+                    if (ka < drel) bw = *(const u32x4*)(rrow + ka);
+                    u32x4 aw = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const int u_lo = T::BN - 4 - kb2 * 32 - 8 * g - 4 * hf;
-                const u32x2 x = *(const u32x2*)(slot + u_lo);
-                const uint32_t pr[2] = {__builtin_amdgcn_alignbit(x[1], x[1], 16),  // elements 4g, 4g + 1
-                                        __builtin_amdgcn_alignbit(x[0], x[0], 16)}; // elements 4g + 2, 4g + 3
-#pragma unroll
-                for (int h2 = 0; h2 < 2; h2++) {
-                    uint32_t w = 0;
-#pragma unroll
-                    for (int e = 0; e < 2; e++) {
-                        const int r = 4 * g + 2 * h2 + e;
-                        const bool vis = lim_vis(lim, 0, kb2, r);
-                        const uint32_t v = (pr[h2] >> (16 * e)) & 0xFFFFu;
-                        // masked: the -inf of the dtype; values outside [0, E) came out 0
-                        w |= (vis ? v : (uint32_t)E::kNegInfBits) << (16 * e);
+                    for (int e = 0; e < 8; e += 2) {
+                        const int k1 = min(ka + e, drel - 1), k2 = min(ka + e + 1, drel - 1);
+                        const uint32_t v1 = pcol[k1 * E_];
+                        const uint32_t v2 = pcol[k2 * E_];
+                        const uint32_t keep1 = din && ka + e < drel ? 0xFFFFu : 0u;
+                        const uint32_t keep2 = din && ka + e + 1 < drel ? 0xFFFFu : 0u;
+                        aw[e >> 1] = (v1 & keep1) | ((v2 & keep2) << 16);
                     }
-                    bb[0][kb2][2 * g + h2] = w;
+                    c = E::mma(__builtin_bit_cast(v8, aw), __builtin_bit_cast(v8, bw), c);
+                }
+                return c;
+            };
+            {
+                const f32x16 cf = block(0), cl = block(NBLK - 1);
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int m = acc_row(r, hf);
+                    slot[(m - off) & (T::BN - 1)] = E::narrow(m >= off ? cf[r] : cl[r]);
                 }
             }
+#pragma unroll
+            for (int b = 1; b < NBLK - 1; b++) {
+                const f32x16 c = block(b);
+#pragma unroll
+                for (int r = 0; r < 16; r++) slot[32 * b + acc_row(r, hf) - off] = E::narrow(c[r]);
+            }
+            // element (kb2, r) of the lane: u = BN - 1 - kb2 * 32 - acc_row(r, hf); a group of
+            // four (r = 4g .. 4g + 3) is one aligned 8-byte read, its values in reverse order
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++)
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const int u_lo = T::BN - 4 - kb2 * 32 - 8 * g - 4 * hf;
+                    const u32x2 x = *(const u32x2*)(slot + u_lo);
+                    const uint32_t pr[2] = {__builtin_amdgcn_alignbit(x[1], x[1], 16),  // elements 4g, 4g + 1
+                                            __builtin_amdgcn_alignbit(x[0], x[0], 16)}; // elements 4g + 2, 4g + 3
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; h2++) {
+                        uint32_t w = 0;
+#pragma unroll
+                        for (int e = 0; e < 2; e++) {
+                            const int r = 4 * g + 2 * h2 + e;
+                            const bool vis = lim_vis(lim, qb, kb2, r);
+                            const uint32_t v = (pr[h2] >> (16 * e)) & 0xFFFFu;
+                            // masked: the -inf of the dtype; values outside [0, E) came out 0
+                            w |= (vis ? v : (uint32_t)E::kNegInfBits) << (16 * e);
+                        }
+                        bb[qb][kb2][2 * g + h2] = w;
+                    }
+                }
+        }
     };
     auto load_bias = [&](BiasBits& bb, int j0) __attribute__((always_inline)) {
         if (fused_bias)
@@ -729,17 +730,11 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
             const float mu = m_used[qb] == -INFINITY ? 0.f : m_used[qb];
-            float rs = 0.f;
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    // exp2(-inf) = 0 for a masked key
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, band_term(qb, kb2, r, bb) - mu));
-                    s[qb][kb2][r] = pv;
-                    rs += pv;
-                }
-            l_run[qb] += rs;
+                for (int r = 0; r < 16; r++)  // exp2(-inf) = 0 for a masked key
+                    s[qb][kb2][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, band_term(qb, kb2, r, bb) - mu));
         }
     };
     // (a visible key's term is 0: the same FMA as the fast path, s * c2 - mu)
@@ -759,18 +754,48 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
             const float mu = m_used[qb] == -INFINITY ? 0.f : m_used[qb];
-            float rs = 0.f;
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const float pv = lim_vis(lim, qb, kb2, r)
-                                         ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, -mu)) : 0.f;
-                    s[qb][kb2][r] = pv;
-                    rs += pv;
-                }
-            l_run[qb] += rs;
+                for (int r = 0; r < 16; r++)
+                    s[qb][kb2][r] = lim_vis(lim, qb, kb2, r)
+                                        ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][r], p.c2, -mu)) : 0.f;
         }
+    };
+
+    // P in the dtype, as the B operand of O^T += V^T P^T: step t (16 keys) of row block
+    // qb holds the exponentials of S^T registers [t / 2][8 (t % 2) .. + 7]
+    auto p_step = [&](const STile& s, int qb, int t) __attribute__((always_inline)) {
+        v8 x;
+#pragma unroll
+        for (int e = 0; e < 8; e++) x[e] = E::to_elem(s[qb][t >> 1][8 * (t & 1) + e]);
+        return x;
+    };
+    // Row sums of a tile's weights, one fixed order whatever the path: per 32-key block a
+    // chain over the block's two steps, pairs in order, then a tree over the blocks into l.
+    // bfloat16: the sum of the rounded weights the PV MFMA uses (one v_dot2 with (1, 1)
+    // per pair), so l normalises exactly the weights O was built from. IEEE half: the
+    // fp32 exponentials (pair sums of half values would lose those below the half
+    // normal range).
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    auto sum_pair = [&](float acc, const STile& s, const v8& pt, int qb, int t, int i) __attribute__((always_inline)) {
+        if constexpr (BF) {
+            // (the pair is built from its two elements: taking it as a 32-bit word of the
+            // bit-cast vector has compiled to the first pair for every i)
+            const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+            const bf16x2 x = {pt[2 * i], pt[2 * i + 1]};
+            return __builtin_amdgcn_fdot2_f32_bf16(x, one2, acc, false);
+        } else {
+            acc += s[qb][t >> 1][8 * (t & 1) + 2 * i];
+            return acc + s[qb][t >> 1][8 * (t & 1) + 2 * i + 1];
+        }
+    };
+    auto sums_into_l = [&](float (&rs)[T::NKB], int qb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int w = 1; w < T::NKB; w *= 2)
+#pragma unroll
+            for (int kb2 = 0; kb2 + w < T::NKB; kb2 += 2 * w) rs[kb2] += rs[kb2 + w];
+        l_run[qb] += rs[0];
     };
 
     // which rows take the remainder MFMA for the tile whose exponentials were just added to l
@@ -809,26 +834,62 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
         if (!dv_ok) w = u32x4{0u, 0u, 0u, 0u};
         return __builtin_bit_cast(v8, w);
     };
-    // O^T += V^T P^T, 16 keys per MFMA step. bf16 P carries a 2^-9 relative
-    // rounding error; for a row whose normaliser is still small (few keys hold
-    // its weight) that error can reach the output tolerance, so such rows also
-    // feed the remainder P - bf16(P) through a second MFMA. A row with
+    // bf16 P carries a 2^-9 relative rounding error; for a row whose normaliser is
+    // still small (few keys hold its weight) that error can reach the output
+    // tolerance, so such rows also feed the remainder P - bf16(P) through the MFMA
+    // (after the tile's main product; its rounded weights join l). A row with
     // normaliser l (max weight 1) has at least l effective keys, and the error
     // shrinks like 2^-9 / sqrt(3 l); rows at or above kLoThresh skip it.
-    auto pv = [&](const char* vl, STile& s) __attribute__((always_inline)) {
+    auto pv_rem = [&](const char* vl, const STile& s) __attribute__((always_inline)) {
+        if constexpr (BF) {
+            // rare: only while some row of the wave has a small normaliser
+            asm volatile("; P remainder" ::: "memory");
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++) {
+                float rs[T::NKB];
+#pragma unroll
+                for (int kb2 = 0; kb2 < T::NKB; kb2++) rs[kb2] = 0.f;
+#pragma unroll
+                for (int t = 0; t < T::BN / 16; t++) {
+                    const v8 pt = p_step(s, qb, t);
+                    v8 ptl;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        const float pvv = s[qb][t >> 1][8 * (t & 1) + e];
+                        ptl[e] = E::to_elem(need_lo[qb] ? pvv - (float)pt[e] : 0.f);
+                    }
+#pragma unroll
+                    for (int dt = 0; dt < ODT; dt++) o[qb][dt] = E::mma(vfrag(vl, t, dt0 + dt), ptl, o[qb][dt]);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) rs[t >> 1] = sum_pair(rs[t >> 1], s, ptl, qb, t, i);
+                }
+                sums_into_l(rs, qb);  // (zero for the rows that skip it)
+            }
+        }
+    };
+    // O^T += V^T P^T, 16 keys per MFMA step, with P formed and summed into l step by
+    // step; then the remainder test on the updated l
+    auto pv = [&](const char* vl, const STile& s) __attribute__((always_inline)) {
+        float rs[T::NQB][T::NKB];
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++)
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++) rs[qb][kb2] = 0.f;
 #pragma unroll
         for (int t = 0; t < T::BN / 16; t++) {
             v8 pt[T::NQB];
 #pragma unroll
-            for (int qb = 0; qb < T::NQB; qb++)
-#pragma unroll
-                for (int e = 0; e < 8; e++) pt[qb][e] = E::to_elem(s[qb][t >> 1][8 * (t & 1) + e]);
+            for (int qb = 0; qb < T::NQB; qb++) pt[qb] = p_step(s, qb, t);
 #pragma unroll
             for (int dt = 0; dt < ODT; dt++) {
                 const v8 a = vfrag(vl, t, dt0 + dt);
 #pragma unroll
                 for (int qb = 0; qb < T::NQB; qb++) o[qb][dt] = E::mma(a, pt[qb], o[qb][dt]);
             }
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) rs[qb][t >> 1] = sum_pair(rs[qb][t >> 1], s, pt[qb], qb, t, i);
         }
         if constexpr (D != 16) {
             // Order: the reads of two V^T fragments ahead of the MFMA that uses the first
@@ -844,27 +905,10 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
             }
             __builtin_amdgcn_sched_group_barrier(0x008, T::NQB * AHEAD, 1);
         }
-        if (BF && any_lo) {
-            // rare: the remainder P - bf16(P) of the small-normaliser rows, accumulated in place
-            asm volatile("; P remainder" ::: "memory");
 #pragma unroll
-            for (int t = 0; t < T::BN / 16; t++) {
-                v8 ptl[T::NQB];
-#pragma unroll
-                for (int qb = 0; qb < T::NQB; qb++)
-#pragma unroll
-                    for (int e = 0; e < 8; e++) {
-                        const float pvv = s[qb][t >> 1][8 * (t & 1) + e];
-                        ptl[qb][e] = E::to_elem(need_lo[qb] ? pvv - (float)E::to_elem(pvv) : 0.f);
-                    }
-#pragma unroll
-                for (int dt = 0; dt < ODT; dt++) {
-                    const v8 a = vfrag(vl, t, dt0 + dt);
-#pragma unroll
-                    for (int qb = 0; qb < T::NQB; qb++) o[qb][dt] = E::mma(a, ptl[qb], o[qb][dt]);
-                }
-            }
-        }
+        for (int qb = 0; qb < T::NQB; qb++) sums_into_l(rs[qb], qb);
+        lo_decision();
+        if (BF && any_lo) pv_rem(vl, s);
     };
 
     // ---- main loop over key tiles ----
@@ -922,20 +966,273 @@ __global__ void __launch_bounds__(256, Tile<D>::WG_PER_CU) attn_fwd_kernel(const
             if (fast) exp_fast(s);
             else if (banded) exp_band(s, bb);
             else exp_mask(s, lim);
-            lo_decision();
             pv(vstage(st), s);
         }
         // tiles issued after kb+1: kb+2 .. min(kb+PREFETCH, kb_end-1)
         wait_tiles_after_next(min(kb + T::PREFETCH, kb_end - 1) - (kb + 1));
         __syncthreads();
     };
+    // ---- software-pipelined run over the leading tiles that no wave of the work-group masks ----
+    // Iteration r (K of tile r+1 and V of tile r in LDS): the MFMAs form S^T of tile r+1
+    // while the VALU turns tile r's scores into exponentials (stage A), then the MFMAs add
+    // tile r's P V to O while the VALU converts P, sums it into l and forms the row maxima
+    // of tile r+1 (stage B). The per-row arithmetic is tile_step's, in the same order, so
+    // a row's result does not depend on which tiles take this run. K runs one tile ahead
+    // of V in the ring: with PF = PREFETCH, iteration r loads K of tile r+1+PF into the
+    // slot tile r's K left and V of tile r+PF into the slot of tile r-1's V. The two S^T
+    // tiles swap registers every iteration, so no accumulator is copied.
+    // Only without the causal mask and the relative bias: there the run covers each row
+    // tile's whole key range. With them every row tile ends its run within a few tiles of
+    // the diagonal or the band, and the run's last step (which spills registers) plus the
+    // hand-over to tile_step cost more than the run saves (varlen causal GQA, 8 sequences
+    // of 512 .. 8192 tokens: +10% time).
+    constexpr bool PIPE = (D == 64 || D == 128) && (T::NB == 2 || T::NB == 4) && !BIAS && !CAUSAL;
+    constexpr int PF = T::PREFETCH;
+    int nf = 0;  // tiles of the run (wave-uniform)
+    if (PIPE && kb_begin < kb_end && p.c2 > 0.f) {
+        const int wg_lo = row0 / gp;  // the work-group's first query: the most restrictive row
+        int lim = k_len / T::BN;      // tiles inside the key range
+        if (CAUSAL) {
+            const int x = wg_lo + delta + 1;  // tile kb is below every diagonal iff (kb + 1) BN <= x
+            lim = min(lim, x > 0 ? x / T::BN : 0);
+        }
+        if (BIAS) {
+            const int x = wg_lo + delta - p.E + 1;  // and before every row's band
+            lim = min(lim, x > 0 ? x / T::BN : 0);
+        }
+        nf = max(0, min(kb_end, lim) - kb_begin);
+        // when tile_step takes over, let it start at ring stage 0 (it addresses the ring
+        // with literal stages): the last nf % NB tiles of the run go to it instead
+        if (nf < kb_end - kb_begin) nf -= nf % T::NB;
+    }
+    const int ntl = kb_end - kb_begin;  // tiles of this work-group's key range
+    // the row maxima of an unmasked tile (raw scores; scaled when committed)
+    float mx_next[T::NQB];
+    auto raw_max = [&](const STile& s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[qb][kb2][r]);
+            mx_next[qb] = partner_max(mx) * p.c2;
+        }
+    };
+    // Commit the maxima; only a row max that grew can call for a rescale (after one,
+    // m_run <= m_used + kTau holds until m_run grows) or make the normaliser relative to
+    // the max fall (lo_check: the remainder test is due).
+    bool lo_check = true;
+    auto commit_max = [&]() __attribute__((always_inline)) {
+        bool grew = false;
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) grew = grew || mx_next[qb] > m_run[qb];
+        if (__any(grew)) {
+            asm volatile("; row max grew" ::: "memory");
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++) m_run[qb] = fmaxf(m_run[qb], mx_next[qb]);
+            update_used_max();
+            rescale_acc();
+            lo_check = true;
+        }
+    };
+    // after a tile's sums: the remainder test (tile_step's, skipped while it cannot pass)
+    auto lo_step = [&](const char* vl, const STile& s) __attribute__((always_inline)) {
+        if (BF && lo_check) {
+            lo_decision();
+            if (any_lo) pv_rem(vl, s);
+            else lo_check = false;
+        }
+    };
+    // The two stages are written in issue order, one K or V fragment at a time: its
+    // MFMAs (one per row block), the LDS reads of a later fragment and a share of the
+    // VALU work, each step fenced by a scheduling barrier, so the VALU work runs in the
+    // shadow of the MFMAs before it and every fragment is read a few steps ahead of use.
+    auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+    // stage A: S^T of the next tile (K fragments from LDS); exponentials of the current one
+    auto stage_a = [&](const char* kl, STile& sn, STile& sc) __attribute__((always_inline)) {
+        constexpr int NM = T::NKB * T::NC;    // fragment steps
+        constexpr int EPM = 16 * T::NKB / NM; // exponentials per step and row block
+        constexpr int AH = T::NC < 4 ? T::NC : 4;  // fragments read ahead
+        auto kread = [&](int g) __attribute__((always_inline)) {
+            return *(const v8*)(kl + k_granule<D>((g / T::NC) * 32 + l32, 2 * (g % T::NC) + hf) * 16);
+        };
+        v8 ka[NM];
+#pragma unroll
+        for (int g = 0; g < AH; g++) ka[g] = kread(g);
+        fence();
+#pragma unroll
+        for (int g = 0; g < NM; g++) {
+            const int kb2 = g / T::NC, c = g % T::NC;
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++)
+                sn[qb][kb2] = E::mma(ka[g], qf[qb][c], c == 0 ? f32x16{} : sn[qb][kb2]);
+            if (g + AH < NM) ka[g + AH] = kread(g + AH);
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++)
+#pragma unroll
+                for (int e = g * EPM; e < (g + 1) * EPM; e++)
+                    sc[qb][e / 16][e % 16] =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][e / 16][e % 16], p.c2, -m_used[qb]));
+            fence();
+        }
+    };
+    // stage B: P V of the current tile (V^T fragments from LDS); P in the dtype, its sums
+    // into l (tile_step's order) and the row maxima of the next tile
+    auto stage_b = [&](const char* vl, const STile& sn, const STile& sc, bool with_max) __attribute__((always_inline)) {
+        constexpr int NTS = T::BN / 16;         // 16-key steps
+        constexpr int NM = NTS * ODT;           // fragment steps
+        constexpr int AH = 2;                   // fragments read ahead
+        constexpr int CPM = 8 / ODT;            // conversions of the next step per fragment step
+        constexpr int MPM = 16 * T::NKB / NM;   // maxima per fragment step and row block
+        v8 pt[T::NQB][NTS];
+        auto cvt = [&](int qb, int t, int e) __attribute__((always_inline)) {
+            pt[qb][t][e] = E::to_elem(sc[qb][t >> 1][8 * (t & 1) + e]);
+        };
+        float rs[T::NQB][T::NKB];  // row sums per 32-key block, as in pv
+        float mx[T::NQB];
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) {
+            mx[qb] = -INFINITY;
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++) rs[qb][kb2] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) cvt(qb, 0, e);
+        }
+        v8 va[NM];
+#pragma unroll
+        for (int g = 0; g < AH; g++) va[g] = vfrag(vl, g / ODT, dt0 + g % ODT);
+        fence();
+#pragma unroll
+        for (int g = 0; g < NM; g++) {
+            const int t = g / ODT, dt = g % ODT;
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++) o[qb][dt] = E::mma(va[g], pt[qb][t], o[qb][dt]);
+            if (g + AH < NM) va[g + AH] = vfrag(vl, (g + AH) / ODT, dt0 + (g + AH) % ODT);
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++) {
+                if (t + 1 < NTS)
+#pragma unroll
+                    for (int e = dt * CPM; e < (dt + 1) * CPM; e++) cvt(qb, t + 1, e);
+                // the sums of step t (its 4 pairs over the step's fragments)
+#pragma unroll
+                for (int i = dt * 4 / ODT; i < (dt + 1) * 4 / ODT; i++)
+                    rs[qb][t >> 1] = sum_pair(rs[qb][t >> 1], sc, pt[qb][t], qb, t, i);
+                if (with_max)
+#pragma unroll
+                    for (int e = g * MPM; e < (g + 1) * MPM; e++) mx[qb] = fmaxf(mx[qb], sn[qb][e / 16][e % 16]);
+            }
+            fence();
+        }
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) {
+            sums_into_l(rs[qb], qb);
+            if (with_max) mx_next[qb] = partner_max(mx[qb]) * p.c2;
+        }
+    };
+    // The work-group barrier of the run. Each wave has waited for exactly the loads the
+    // next iteration reads (s_waitcnt vmcnt) and its LDS reads of the stages about to be
+    // refilled have all returned (their MFMAs consumed them), so a plain s_barrier
+    // suffices; __syncthreads would add a release fence, i.e. a wait for every load in
+    // flight, including the tiles loaded further ahead. The empty asm statements keep
+    // the compiler from moving LDS accesses across it.
+    auto sync_run = []() __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // s_waitcnt vmcnt(n * LOADS): at most n later K or V tile loads of this wave in flight
+    auto wait_halves = [&](int n) __attribute__((always_inline)) {
+        constexpr int L = T::LOADS;
+        static_assert(2 * (PF - 1) * L < 64, "vmcnt field");
+        if (n <= 0) wait_vm_loads<0>();
+        else if (PF < 2 || n == 1) wait_vm_loads<L>();
+        else if (n == 2) wait_vm_loads<2 * L>();
+        else if (n == 3) wait_vm_loads<(PF > 2 ? 3 : 2) * L>();
+        else wait_vm_loads<(PF > 2 ? 4 : 2) * L>();
+    };
+    static_assert(PF <= 3, "wait_halves covers up to four later loads");
+    // K and V loads iteration i of the run issues (when the tile exists)
+    auto iter_loads = [&](int i) __attribute__((always_inline)) {
+        return (i + 1 + PF < ntl ? 1 : 0) + (i + PF < ntl ? 1 : 0);
+    };
+    // iteration r uses ring stage st = r % NB: a literal with two stages (the loop is
+    // unrolled by two for the S^T tiles anyway), else a run-time value (uniform stage
+    // bases that the per-lane LDS addresses add)
+    auto pipe_iter = [&](int r, STile& sc, STile& sn, int st) __attribute__((always_inline)) {
+        const int kb = kb_begin + r;
+        // K of tile r+1+PF goes to K stage st, V of tile r+PF to V stage (st+PF) % NB
+        if (r + 1 + PF < ntl) issue_tile(kbase, kb + 1 + PF, kstage(st), false);
+        if (r + PF < ntl) issue_tile(vbase, kb + PF, vstage((st + PF) & (T::NB - 1)), true);
+        stage_a(kstage((st + 1) & (T::NB - 1)), sn, sc);
+        stage_b(vstage(st), sn, sc, true);
+        lo_step(vstage(st), sc);
+        commit_max();
+        // K of tile r+2 and V of tile r+1 must have landed: they were issued before the
+        // loads of iterations max(0, r+2-PF) .. r
+        int after = 0;
+#pragma unroll
+        for (int j = 0; j < PF - 1; j++)
+            if (r - j >= 0) after += iter_loads(r - j);
+        wait_halves(after);
+        sync_run();
+    };
+    auto pipe_last = [&](int r, STile& sc, int st) __attribute__((always_inline)) {
+        const int kb = kb_begin + r;
+        if (r + PF < ntl) issue_tile(vbase, kb + PF, vstage((st + PF) & (T::NB - 1)), true);
+        exp_fast(sc);
+        fence();
+        stage_b(vstage(st), sc, sc, false);
+        lo_step(vstage(st), sc);
+        // the tile_step path keeps its own load order: start it with nothing in flight
+        wait_vm_all();
+        __syncthreads();
+    };
+
     if (kb_begin < kb_end) {
         const int first_end = min(kb_begin + T::PREFETCH, kb_end);
         for (int j = kb_begin; j < first_end; j++) issue(j, j - kb_begin);
         wait_tiles_after_next(first_end - 1 - kb_begin);  // tile kb_begin has landed
         __syncthreads();
+        int kb = kb_begin;
+        if constexpr (PIPE) {
+            if (nf > 0) {
+                STile sa, sb;
+                // prologue: K of tile PF goes out; S^T and maxima of tile 0; then K of tile 1
+                // (issued before V of tile 1 .. PF-1 and K of tile 2 .. PF) must land
+                if (PF < ntl) issue_tile(kbase, kb_begin + PF, kstage(PF % T::NB), false);
+                qk(kstage(0), sa);
+                raw_max(sa);
+                commit_max();
+                {
+                    // issued after K of tile 1: V of tile 1, K and V of tiles 2 .. PF-1, K of tile PF
+                    // (with PF = 1, K of tile 1 is the last load issued)
+                    int after = (PF >= 2 && PF < ntl) ? 1 : 0;
+#pragma unroll
+                    for (int j = 1; j < PF; j++) after += (j >= 2 && j < ntl ? 1 : 0) + (j < ntl ? 1 : 0);
+                    wait_halves(after);
+                }
+                sync_run();
+                // unrolled by two: the S^T tiles alternate in step, so only one is live at the
+                // loop's back edge
+                // (r is even at each first call below)
+                auto stage_of = [](int r, int lit) { return T::NB == 2 ? lit : r & (T::NB - 1); };
+                int r = 0;
+                for (; r + 2 < nf; r += 2) {
+                    pipe_iter(r, sa, sb, stage_of(r, 0));
+                    pipe_iter(r + 1, sb, sa, stage_of(r + 1, 1));
+                }
+                if (r + 1 < nf) {
+                    pipe_iter(r, sa, sb, stage_of(r, 0));
+                    pipe_last(r + 1, sb, stage_of(r + 1, 1));
+                } else {
+                    pipe_last(r, sa, stage_of(r, 0));
+                }
+                kb = kb_begin + nf;
+            }
+        }
         // unrolled over the ring stages (NB <= 5)
-        for (int kb = kb_begin; kb < kb_end; kb += T::NB) {
+        for (; kb < kb_end; kb += T::NB) {
             tile_step(kb, 0);
             if (T::NB > 1 && kb + 1 < kb_end) tile_step(kb + 1, 1 % T::NB);
             if (T::NB > 2 && kb + 2 < kb_end) tile_step(kb + 2, 2 % T::NB);
@@ -993,15 +1290,24 @@ template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT, bool 
 hipError_t launch_one(const FwdParams& p, hipStream_t s) {
     const void* fn = (const void*)attn_fwd_kernel<D, BF, CAUSAL, VARLEN, BIAS, SPLIT, DSPLIT>;
     // bias instances may carry the fused producer's rows past the ring
-    constexpr unsigned lds_max = BIAS ? kLdsBytesPerCU : Tile<D>::LDS;
-    static const hipError_t attr =
-        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
-    if (attr != hipSuccess) return attr;
-    const unsigned lds = Tile<D>::LDS + (BIAS ? (unsigned)p.lds_extra : 0u);
+    using T = Tile<D, CAUSAL>;
+    constexpr unsigned lds_max = BIAS ? kLdsBytesPerCU / T::WG_PER_CU : T::LDS;
+    // the LDS limit is raised once per device; a failure is returned and tried again on
+    // the next call (only success is remembered)
+    static std::atomic<uint64_t> attr_set{0};  // bit d: done on device d
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit == 0 || !(attr_set.load(std::memory_order_acquire) & bit)) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
+        if (e != hipSuccess) return e;
+        attr_set.fetch_or(bit, std::memory_order_acq_rel);
+    }
+    const unsigned lds = T::LDS + (BIAS ? (unsigned)p.lds_extra : 0u);
     if (lds > lds_max) return hipErrorInvalidValue;
     FwdParams pp = p;
     void* args[] = {(void*)&pp};
-    return hipLaunchKernel(fn, dim3(p.nblocks), dim3(Tile<D>::NT), args, lds, s);
+    return hipLaunchKernel(fn, dim3(p.nblocks), dim3(T::NT), args, lds, s);
 }
 
 typedef hipError_t (*FwdLauncher)(const FwdParams&, hipStream_t);

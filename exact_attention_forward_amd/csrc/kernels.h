@@ -12,21 +12,32 @@ __host__ __device__ constexpr int head_dim_class(int d) {
     return d <= 16 ? 16 : d <= 64 ? 64 : d <= 128 ? 128 : 256;
 }
 
-// Work-group geometry of the forward kernel for head-dim class D: 4 waves of 64
+// Work-group geometry of the forward kernel for head-dim class D: NW waves of 64
 // lanes; each wave owns NQB blocks of 32 query rows (one MFMA 32x32 output column
 // block per row block); BN keys per K/V tile.
 
 __host__ __device__ constexpr int tile_nqb(int /*D*/) { return 1; }
-__host__ __device__ constexpr int tile_bm(int D) { return 4 * 32 * tile_nqb(D); }
+// Waves per work-group: eight at head-dim class 128 without the causal mask, so a 256-row
+// work-group shares each K / V tile it brings into LDS (half the L2 -> LDS traffic per FLOP
+// of four waves: [1,20480,56,128] bf16 forward -3.9% time with the pipelined key loop);
+// four elsewhere. Causal row tiles keep 128 rows: the diagonal stays finer and unequal
+// varlen sequences balance better (the varlen causal GQA + rel_bias workload measured +4.9%
+// time with 256-row tiles).
+__host__ __device__ constexpr int tile_nw(int D, bool causal) { return D == 128 && !causal ? 8 : 4; }
+__host__ __device__ constexpr int tile_bm(int D, bool causal) { return tile_nw(D, causal) * 32 * tile_nqb(D); }
 // Keys per K/V tile: 64; 128 at head-dim class 16, where a tile's MFMA work is smallest
 // (measured c4b -6% time against 64; at class 64 the same measured +3% on c4a).
 __host__ __device__ constexpr int tile_bn(int D) { return D <= 16 ? 128 : 64; }
-// Work-groups resident per CU: two up to head dim 128; at 256 a wave needs more
-// than 256 registers, so one.
-__host__ __device__ constexpr int tile_wg_per_cu(int D) { return D <= 128 ? 2 : 1; }
+// Work-groups resident per CU: two of four waves up to head dim 128; one of eight waves
+// at 128 without the causal mask; one at 256, where a wave needs more than 256 registers.
+__host__ __device__ constexpr int tile_wg_per_cu(int D, bool causal) {
+    return D <= 64 || (D == 128 && causal) ? 2 : D == 128 ? 1 : 1;
+}
 // K/V tiles loaded ahead of the one being consumed (the LDS ring has one more stage):
-// one, in a ring of at most 64 KB up to head dim 128 and 128 KB at 256 (measured at 256
-// against 32-key tiles three ahead: prefill c5a -16%, decode c5b -10% time)
+// one, in a ring of at most 64 KB up to head dim 64 and 128 KB at 256 (measured at 256
+// against 32-key tiles three ahead: prefill c5a -16%, decode c5b -10% time). At 128
+// (eight waves, 64 KB) three tiles ahead in a 128 KB ring measured 2% slower on the
+// [1,20480,56,128] bf16 forward.
 __host__ __device__ constexpr int tile_prefetch(int /*D*/) { return 1; }
 // LDS of the K/V ring: (PREFETCH + 1) stages, each a K and a V tile of BN x D 16-bit values
 __host__ __device__ constexpr int tile_ring_bytes(int D) { return (tile_prefetch(D) + 1) * 2 * tile_bn(D) * D * 2; }

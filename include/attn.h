@@ -33,7 +33,8 @@
  *   - Any violated requirement returns an error code, launches nothing and
  *     writes nothing. No other kernel is ever substituted.
  *   - The library keeps no state between calls beyond a lazily cached device
- *     property; calls are reentrant.
+ *     property (the compute-unit count of each device) and, per kernel and device,
+ *     whether its LDS limit has been raised; calls are reentrant.
  */
 #ifndef MI355_ATTN_H
 #define MI355_ATTN_H
@@ -109,7 +110,9 @@ typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1 } attn_dtype_t;
  *   of 8 is the range the TabPFN issue thread gives for FA4 on sm_90);
  *   D = Dv = 64, 128 and 256 run at full efficiency, other pairs on the kernel
  *   of the next size up (16, 64, 128 or 256) with the extra columns zero.
- * Limits: Hkv * max(D, Dv) <= 2^23; sizes must keep every element count below 2^62.
+ * Limits: one K or V tile must span at most 2^30 bytes, i.e. Hkv * max(D, Dv) <= 2^23
+ *   (2^22 when max(D, Dv) <= 16, where a tile holds 128 keys instead of 64); sizes must
+ *   keep every element count below 2^62.
  */
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                        int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale,
@@ -146,7 +149,8 @@ attn_status_t attn_fwd_rel_proj(const void* q, const void* k, const void* v, voi
                                 size_t workspace_bytes, void* stream);
 
 /*
- * attn_check_args -- attn_fwd's validation alone, on the host, with no GPU call.
+ * attn_check_args -- attn_fwd's validation alone, on the host, with no GPU work
+ * (not from the pages: a check a caller can make before enqueueing).
  * Same arguments as attn_fwd minus the stream; returns the code attn_fwd would
  * return before launching anything. Pointers are only checked for NULL and
  * alignment, never dereferenced.
@@ -162,21 +166,30 @@ attn_status_t attn_check_args(const void* q, const void* k, const void* v, void*
 /*
  * attn_num_splits -- the number of key-range splits attn_fwd uses for these
  * sizes and this request (num_splits <= 0: the heuristic; otherwise the
- * request clamped). is_varlen selects the meaning of Sq/Sk as in attn_fwd.
- * Pure host function. Returns >= 1, or 0 for invalid sizes.
+ * request clamped). causal and is_varlen as in attn_fwd (causal changes the
+ * work-group shape at head-dim class 128, hence the grid the heuristic sees).
+ * Host function, no GPU work (it reads the current device's compute-unit count
+ * once). Returns >= 1, or 0 for invalid sizes. Not from the pages: the split
+ * count is this library's scheduling choice; every count gives the same result
+ * up to rounding.
  * Heuristic: split only when the unsplit grid has fewer work-groups than fit
- * on the chip at once (256 compute units x 2 work-groups each for D <= 128,
- * x 1 for D = 256); then use n = floor(that / work-groups) splits (one wave of
- * work-groups fills the chip), times r = min(8, floor(key blocks / n / 64)) when
- * r > 1 (several waves while each split keeps at least 64 key blocks), never
- * fewer than 4 key blocks per split (64 keys per block; 128 for D <= 16) and
- * never more than ATTN_MAX_SPLITS splits.
+ * on the device at once (compute units of the current device -- 256 on a full
+ * MI355X, also used when no device is visible -- times the work-groups resident
+ * per CU: 2 up to head-dim class 64 and for causal class 128, 1 for non-causal
+ * class 128 (eight-wave work-groups) and for class 256); then use
+ * n = floor(that / work-groups) splits (one wave of work-groups fills the device),
+ * times r = min(8, floor(key blocks / n / 64)) when r > 1 (several waves while
+ * each split keeps at least 64 key blocks), never fewer than 4 key blocks per
+ * split (64 keys per block; 128 for D <= 16) and never more than
+ * ATTN_MAX_SPLITS splits. Rows per work-group: 256 for non-causal class 128,
+ * 128 otherwise.
  */
-int attn_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int is_varlen,
+int attn_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int causal, int is_varlen,
                     int max_seqlen_q, int max_seqlen_k, int pack_gqa, int num_splits);
 
 /*
- * attn_fwd_workspace_size -- bytes of workspace attn_fwd needs for `num_splits`
+ * attn_fwd_workspace_size -- (not from the pages: the partials' storage of this
+ * library's split-KV path) bytes of workspace attn_fwd needs for `num_splits`
  * splits (0 when num_splits <= 1). Layout: fp32 O partials
  * [num_splits, rows_q, Hq, Dv] followed by fp32 LSE partials
  * [num_splits, <lse layout>] (rows_q = B*Sq dense, Sq = total_q varlen).
@@ -184,7 +197,9 @@ int attn_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, int i
 size_t attn_fwd_workspace_size(int B, int Sq, int Hq, int Dv, int is_varlen, int num_splits);
 
 /*
- * attn_combine -- LSE-weighted merge of split partials (the split-KV combine).
+ * attn_combine -- LSE-weighted merge of split partials (the split-KV combine that
+ * the returned LSE makes possible outside the kernel: TabPFN issue #1235, closing
+ * comment; "split-KV combine" in the tml-fa4 page's introduction).
  *   o_partial [num_splits, rows_q, Hq, Dv] fp32, lse_partial [num_splits, <lse layout>] fp32,
  *   each split's O normalised within the split, an empty split marked by lse = -inf.
  *   M = max_s lse_s;  lse = M + ln sum_s exp(lse_s - M);  out = sum_s exp(lse_s - lse) o_s
@@ -198,10 +213,10 @@ attn_status_t attn_combine(const float* o_partial, const float* lse_partial, int
                            void* out, float* lse, int B, int Sq, int Hq, int Dv, int is_varlen,
                            attn_dtype_t dtype, void* stream);
 
-/* Human-readable name of a status code (static storage; never NULL). */
+/* Human-readable name of a status code (static storage; never NULL). Not from the pages. */
 const char* attn_status_string(attn_status_t status);
 
-/* Library version string, e.g. "mi355-attn 0.1.0 gfx950". */
+/* Library version string, e.g. "mi355-attn 0.2.0 gfx950". Not from the pages. */
 const char* attn_version(void);
 
 #ifdef __cplusplus

@@ -118,7 +118,7 @@ def test_invalid_calls(lib, over, code):
 
 def test_workspace_and_splits(lib):
     # split with a large enough workspace is accepted
-    ns = lib.attn_num_splits(1, 257, 100000, 8, 8, 128, 128, 0, 0, 0, -1, 4)
+    ns = lib.attn_num_splits(1, 257, 100000, 8, 8, 128, 128, 0, 0, 0, 0, -1, 4)
     assert ns == 4
     need = lib.attn_fwd_workspace_size(1, 257, 8, 128, 0, 4)
     assert need == 4 * 257 * 8 * 129 * 4
@@ -126,29 +126,28 @@ def test_workspace_and_splits(lib):
     assert check(lib, ns=4, Sk=100000, ws=A + 4, ws_bytes=need) == CODE["ATTN_ERR_MISALIGNED"]
     assert lib.attn_fwd_workspace_size(1, 257, 8, 128, 0, 1) == 0
     # requested splits are clamped to the number of key blocks and to 256
-    assert lib.attn_num_splits(1, 10, 200, 1, 1, 64, 64, 0, 0, 0, -1, 50) == ceil_div(200, bn(64))
-    assert lib.attn_num_splits(1, 10, 10**6, 1, 1, 64, 64, 0, 0, 0, -1, 1000) == 256
+    assert lib.attn_num_splits(1, 10, 200, 1, 1, 64, 64, 0, 0, 0, 0, -1, 50) == ceil_div(200, bn(64))
+    assert lib.attn_num_splits(1, 10, 10**6, 1, 1, 64, 64, 0, 0, 0, 0, -1, 1000) == 256
     # heuristic: no split when the grid already covers the chip
-    assert lib.attn_num_splits(1, 20480, 20480, 56, 56, 128, 128, 0, 0, 0, -1, 0) == 1
-    assert lib.attn_num_splits(1, 1024, 20480, 4, 4, 128, 128, 0, 0, 0, -1, 0) == heuristic(32, 20480, 128)
-    assert lib.attn_num_splits(1, 2048, 20480, 2, 1, 256, 256, 0, 0, 0, -1, 0) == heuristic(32, 20480, 256)
+    assert lib.attn_num_splits(1, 20480, 20480, 56, 56, 128, 128, 0, 0, 0, 0, -1, 0) == 1
+    assert lib.attn_num_splits(1, 1024, 20480, 4, 4, 128, 128, 0, 0, 0, 0, -1, 0) == \
+        heuristic(4 * ceil_div(1024, bm(128)), 20480, 128)
+    assert lib.attn_num_splits(1, 2048, 20480, 2, 1, 256, 256, 0, 0, 0, 0, -1, 0) == heuristic(32, 20480, 256)
     # decode B=32, one KV head, 8:1 packed into one row tile: 32 work-groups
-    assert lib.attn_num_splits(32, 1, 131072, 8, 1, 256, 256, 0, 0, 0, -1, 0) == heuristic(32, 131072, 256)
-    # short query, long keys: 6 heads x ceil(1000 / BM) row tiles
-    wg = 6 * ceil_div(1000, BM)
-    assert lib.attn_num_splits(1, 1000, 10**6, 6, 6, 64, 64, 0, 0, 0, -1, 0) == heuristic(wg, 10**6, 64)
+    assert lib.attn_num_splits(32, 1, 131072, 8, 1, 256, 256, 0, 0, 0, 0, -1, 0) == heuristic(32, 131072, 256)
+    # short query, long keys: 6 heads x ceil(1000 / rows per work-group) row tiles
+    wg = 6 * ceil_div(1000, bm(64))
+    assert lib.attn_num_splits(1, 1000, 10**6, 6, 6, 64, 64, 0, 0, 0, 0, -1, 0) == heuristic(wg, 10**6, 64)
     # never fewer than 4 key blocks per split
-    assert lib.attn_num_splits(1, 1, 640, 1, 1, 64, 64, 0, 0, 0, -1, 0) == ceil_div(640, bn(64)) // 4
-    assert lib.attn_num_splits(1, 1, 640, 1, 1, 256, 256, 0, 0, 0, -1, 0) == ceil_div(640, bn(256)) // 4
+    assert lib.attn_num_splits(1, 1, 640, 1, 1, 64, 64, 0, 0, 0, 0, -1, 0) == ceil_div(640, bn(64)) // 4
+    assert lib.attn_num_splits(1, 1, 640, 1, 1, 256, 256, 0, 0, 0, 0, -1, 0) == ceil_div(640, bn(256)) // 4
     # a head-dim pair plans like the class of the larger dim
-    assert lib.attn_num_splits(1, 1, 640, 1, 1, 72, 72, 0, 0, 0, -1, 0) == ceil_div(640, bn(128)) // 4
-    assert lib.attn_num_splits(1, 1, 640, 1, 1, 128, 200, 0, 0, 0, -1, 0) == ceil_div(640, bn(256)) // 4
+    assert lib.attn_num_splits(1, 1, 640, 1, 1, 72, 72, 0, 0, 0, 0, -1, 0) == ceil_div(640, bn(128)) // 4
+    assert lib.attn_num_splits(1, 1, 640, 1, 1, 128, 200, 0, 0, 0, 0, -1, 0) == ceil_div(640, bn(256)) // 4
     # varlen sizes come from max_seqlen
-    assert lib.attn_num_splits(4, 400, 400000, 8, 8, 128, 128, 1, 100, 100000, -1, 0) == \
-        heuristic(4 * 8 * ceil_div(100, BM), 100000, 128)
+    assert lib.attn_num_splits(4, 400, 400000, 8, 8, 128, 128, 0, 1, 100, 100000, -1, 0) == \
+        heuristic(4 * 8 * ceil_div(100, bm(128)), 100000, 128)
 
-
-BM = 128  # rows per work-group of the forward kernel
 
 
 def bn(D):
@@ -161,8 +160,14 @@ def ceil_div(a, b):
 
 
 def resident(D):
-    """Work-groups that fit on the chip at once: 256 CUs x 2 (D <= 128) or x 1 (above)."""
-    return 256 * (2 if D <= 128 else 1)
+    """Work-groups that fit on the chip at once: 256 CUs x 2 (head-dim class up to 64) or
+    x 1 (classes 128 and 256)."""
+    return 256 * (2 if D <= 64 else 1)
+
+
+def bm(D):
+    """Rows per work-group: 256 at head-dim class 128 (eight waves), 128 elsewhere."""
+    return 256 if 64 < D <= 128 else 128
 
 
 def heuristic(work_groups, k_len, D):
@@ -209,3 +214,120 @@ def test_rel_proj_validation(lib):
     assert check_rel_proj(lib, B=0, E=512) == 0
     assert check_rel_proj(lib, B=0, D=256, Dv=256, E=256) == 0
     assert check_rel_proj(lib, B=0, D=256, Dv=256, E=1024) == 0
+
+
+@pytest.mark.parametrize("D,hkv_max", [(8, 1 << 19), (16, 1 << 18), (64, 1 << 17), (128, 1 << 16), (256, 1 << 15)])
+def test_tile_bytes_bound_per_class(lib, D, hkv_max):
+    """One K or V tile (128 keys at head-dim class 16, 64 above) of Hkv heads must span at
+    most 2^30 bytes, the fixed out-of-range load offset of the columns past the head dim."""
+    keys = 128 if D <= 16 else 64
+    assert keys * hkv_max * D * 2 == 1 << 30
+    assert check(lib, B=1, Sq=1, Sk=1, Hq=hkv_max, Hkv=hkv_max, D=D, Dv=D) == 0
+    over = hkv_max + 1
+    assert check(lib, B=1, Sq=1, Sk=1, Hq=over, Hkv=over, D=D, Dv=D) == CODE["ATTN_ERR_BAD_SHAPE"]
+    # the larger of D and Dv decides
+    assert check(lib, B=1, Sq=1, Sk=1, Hq=over, Hkv=over, D=8, Dv=D) == CODE["ATTN_ERR_BAD_SHAPE"]
+
+
+def combine(lib, o=A, l=A, ns=2, out=A, lse=A, B=1, Sq=16, Hq=8, Dv=128, varlen=0, dtype=0):
+    """attn_combine with arguments its validation rejects (or no rows): no GPU call."""
+    return lib.attn_combine(o, l, ns, out, lse, B, Sq, Hq, Dv, varlen, dtype, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=5), "ATTN_ERR_BAD_DTYPE"),
+    (dict(B=-1), "ATTN_ERR_BAD_SHAPE"),
+    (dict(Sq=-1), "ATTN_ERR_BAD_SHAPE"),
+    (dict(Hq=0), "ATTN_ERR_BAD_SHAPE"),
+    (dict(Dv=100), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(Dv=0), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(Dv=264), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(ns=0), "ATTN_ERR_BAD_SPLITS"),
+    (dict(ns=257), "ATTN_ERR_BAD_SPLITS"),
+    (dict(o=None), "ATTN_ERR_NULL_POINTER"),
+    (dict(l=None), "ATTN_ERR_NULL_POINTER"),
+    (dict(out=None), "ATTN_ERR_NULL_POINTER"),
+    (dict(o=A + 4), "ATTN_ERR_MISALIGNED"),
+    (dict(l=A + 2), "ATTN_ERR_MISALIGNED"),
+    (dict(out=A + 8), "ATTN_ERR_MISALIGNED"),
+    (dict(lse=A + 1), "ATTN_ERR_MISALIGNED"),
+    (dict(B=1 << 20, Sq=1 << 20, Hq=1 << 20), "ATTN_ERR_BAD_SHAPE"),
+    (dict(B=1 << 16, Sq=1 << 16, Hq=8, Dv=8), "ATTN_ERR_BAD_SHAPE"),  # one work-group per (row, head): > 2^31
+])
+def test_combine_invalid_calls(lib, over, code):
+    assert combine(lib, **over) == CODE[code]
+
+
+def test_combine_nothing_to_do(lib):
+    # no rows: accepted without a launch, NULL buffers included
+    assert combine(lib, B=0, o=None, l=None, out=None, lse=None) == 0
+    assert combine(lib, Sq=0, varlen=1, o=None, l=None, out=None) == 0
+
+
+def _cpu(shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("case,match", [
+    (dict(k=(1, 64, 2, 64)), "k"),                       # head dim differs from q
+    (dict(k=(2, 64, 2, 128)), "k"),                      # batch differs
+    (dict(v=(1, 32, 2, 128)), "v"),                      # keys differ from k
+    (dict(k=(64, 2, 128)), "rank|k and v"),              # rank differs
+    (dict(out=(1, 16, 8, 64)), "out"),
+    (dict(lse=(1, 16, 8)), "lse"),
+    (dict(lse_dtype="bf16"), "lse"),
+    (dict(seqused=(2,)), "seqused_k"),
+    (dict(seqused_dtype="int64"), "seqused_k"),
+    (dict(rel_bias=(15, 8, 256)), "rel_bias"),              # rows differ from B * Sq
+    (dict(), "CUDA"),                                    # all shapes right: the CPU tensors are refused
+])
+def test_binding_rejects_bad_tensors(case, match):
+    """Checks in the Python binding that run before any pointer reaches the library."""
+    import torch
+    q = _cpu((1, 16, 8, 128))
+    k = _cpu(case.get("k", (1, 64, 2, 128)))
+    v = _cpu(case.get("v", (1, 64, 2, 128)))
+    kw = {}
+    if "out" in case:
+        kw["out"] = _cpu(case["out"])
+    if "lse" in case:
+        kw["lse"] = _cpu(case["lse"], torch.float32)
+    if "lse_dtype" in case:
+        kw["lse"] = _cpu((1, 8, 16))
+    if "seqused" in case:
+        kw["seqused_k"] = torch.zeros(case["seqused"], dtype=torch.int32)
+    if "seqused_dtype" in case:
+        kw["seqused_k"] = torch.zeros((1,), dtype=torch.int64)
+    if "rel_bias" in case:
+        kw["rel_bias"] = _cpu(case["rel_bias"])
+    with pytest.raises(ValueError, match=match):
+        fa.attn_fwd(q, k, v, **kw)
+
+
+def test_binding_rejects_bad_varlen_metadata():
+    import torch
+    q = _cpu((30, 8, 64))
+    k = _cpu((40, 8, 64))
+    good = torch.tensor([0, 10, 30], dtype=torch.int32)
+    for cu_q, cu_k, match in (
+            (torch.tensor([0, 10, 30]), good, "cu_seqlens_q"),             # int64 by default
+            (good, torch.tensor([0, 40], dtype=torch.int32), "cu_seqlens_k"),  # B + 1 differs
+            (good, good.view(1, 3), "cu_seqlens_k")):                     # not 1-D
+        with pytest.raises(ValueError, match=match):
+            fa.attn_fwd(q, k, k, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, max_seqlen_q=20, max_seqlen_k=30)
+
+
+def test_binding_combine_rejects_bad_tensors():
+    import torch
+    o_p = torch.zeros((3, 16, 8, 64), dtype=torch.float32)
+    l_p = torch.zeros((3, 1, 8, 16), dtype=torch.float32)
+    out = _cpu((1, 16, 8, 64))
+    with pytest.raises(ValueError, match="lse_partial"):
+        fa.attn_combine(o_p, l_p[:, :, :4], out=out, B=1, Sq=16)
+    with pytest.raises(ValueError, match="rows"):
+        fa.attn_combine(o_p, l_p, out=out, B=2, Sq=16)
+    with pytest.raises(ValueError, match="out"):
+        fa.attn_combine(o_p, l_p, out=_cpu((1, 16, 8, 128)), B=1, Sq=16)
+    with pytest.raises(ValueError, match="CUDA"):
+        fa.attn_combine(o_p, l_p, out=out, B=1, Sq=16)

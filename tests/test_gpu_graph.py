@@ -43,7 +43,7 @@ def test_graph_replays_match_eager(shape):
     qb, kb, vb = _inputs(dtype, B, Sq, Sk, Hq, Hkv, D, seed=4242 + D)
     q, k, v = dev16(qb, dtype), dev16(kb, dtype), dev16(vb, dtype)
     scale = float(np.float32(1.0 / np.sqrt(D)))
-    ns = fa.num_splits(B, Sq, Sk, Hq, Hkv, D, D, requested=ns_req)
+    ns = fa.num_splits(B, Sq, Sk, Hq, Hkv, D, D, causal=causal, requested=ns_req)
     ws_bytes = fa.workspace_size(B, Sq, Hq, D, splits=ns)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(q)

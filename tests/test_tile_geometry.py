@@ -2,8 +2,9 @@
 
 The kernel reads a band tile's bias with one per-lane offset plus immediates and
 builds the fused producer's values in a per-row LDS slot; both lean on bounds of
-its row / key geometry (a 128-row work-group of four 32-row waves, 64-key tiles
-(32-key tiles checked as well), bottom-right causal mask, the band
+its row / key geometry (work-groups of four or eight 32-row waves, i.e. 128 or 256 rows;
+64-key tiles, 128 at head-dim class 16, 32-key tiles checked as well; bottom-right causal
+mask, the band
 0 <= d < E with d = i + (k_len - q_len) - j). This walks that geometry for random
 shapes and checks the bounds:
 
@@ -19,14 +20,12 @@ import numpy as np
 
 from workloads import gen
 
-BM = 128
-
 
 def acc_row(r, hf):
     return 8 * (r >> 2) + 4 * hf + (r & 3)
 
 
-def walk(q_len, k_len, gp, causal, E, BN):
+def walk(q_len, k_len, gp, causal, E, BN, BM=128):
     """Yield (wave rows, j0, lanes) for every band tile of one (batch, head group)."""
     delta = k_len - q_len
     n_rows = q_len * gp
@@ -36,7 +35,7 @@ def walk(q_len, k_len, gp, causal, E, BN):
         i_hi = r_last // gp
         kv_end = min(k_len, i_hi + delta + 1) if causal else k_len
         kv_end = max(kv_end, 0)
-        for wave in range(4):
+        for wave in range(BM // 32):
             w_row = row0 + 32 * wave
             wi_lo = min(w_row, r_last) // gp
             wi_hi = min(w_row + 31, r_last) // gp
@@ -48,9 +47,9 @@ def walk(q_len, k_len, gp, causal, E, BN):
                     yield wi_lo, wi_hi, j0, qi, delta
 
 
-def check_shape(q_len, k_len, gp, causal, E, BN):
+def check_shape(q_len, k_len, gp, causal, E, BN, BM=128):
     nkb = BN // 32
-    for wi_lo, wi_hi, j0, qi, delta in walk(q_len, k_len, gp, causal, E, BN):
+    for wi_lo, wi_hi, j0, qi, delta in walk(q_len, k_len, gp, causal, E, BN, BM):
         assert wi_hi - wi_lo <= 31
         d_b = wi_lo + delta - j0 - (BN - 1)
         for l32 in range(32):
@@ -88,14 +87,17 @@ def test_band_tile_bounds_random_shapes():
         gp = int(rng.choice([1, 2, 4, 8]))
         causal = bool(rng.random() < 0.6)
         E = int(rng.choice([128, 256, 384]))
-        BN = int(rng.choice([64, 32]))
-        check_shape(q_len, k_len, gp, causal, E, BN)
+        BN = int(rng.choice([64, 32, 128]))
+        BM = int(rng.choice([128, 256]))
+        check_shape(q_len, k_len, gp, causal, E, BN, BM)
 
 
 def test_band_tile_bounds_edges():
     # decode rows, q_len > k_len (rows that see nothing), one-key sequences
     for args in [(1, 5000, 8, True, 128, 32), (300, 40, 1, True, 256, 64), (1, 1, 1, False, 128, 64),
-                 (129, 129, 1, True, 128, 64), (64, 2000, 8, False, 384, 64)]:
+                 (129, 129, 1, True, 128, 64), (64, 2000, 8, False, 384, 64),
+                 (257, 257, 1, True, 128, 128), (300, 900, 4, False, 256, 128, 256),
+                 (513, 513, 1, True, 256, 64, 256), (1, 3000, 8, True, 384, 128)]:
         check_shape(*args)
 
 
