@@ -28,8 +28,9 @@ STATUS = {
     4: "ATTN_ERR_UNSUPPORTED_HEAD_DIM", 5: "ATTN_ERR_BAD_GQA", 6: "ATTN_ERR_BAD_REL_EXTENT",
     7: "ATTN_ERR_BAD_VARLEN", 8: "ATTN_ERR_MISALIGNED", 9: "ATTN_ERR_WORKSPACE",
     10: "ATTN_ERR_UNSUPPORTED_COMBO", 11: "ATTN_ERR_HIP", 12: "ATTN_ERR_BAD_SPLITS",
-    13: "ATTN_ERR_BAD_SCALE", 14: "ATTN_ERR_BAD_ARG",
+    13: "ATTN_ERR_BAD_SCALE", 14: "ATTN_ERR_BAD_ARG", 15: "ATTN_ERR_SCRATCH",
 }
+SCRATCH_BYTES = 16 << 20  # ATTN_SCRATCH_BYTES: split partials attn_fwd_noalloc can hold
 CODE = {v: k for k, v in STATUS.items()}
 
 # The exported symbols and their C signatures (kept in step with include/attn.h).
@@ -40,6 +41,8 @@ _Z = ctypes.c_size_t
 SIGNATURES = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _I, _P,
                       _P, _I, _I, _I, _I, _P, _Z, _P]),
+    "attn_fwd_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _I, _P,
+                              _P, _I, _I, _I, _I, _P]),
     "attn_fwd_rel_proj": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _I,
                                _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]),
     "attn_check_args": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _I,
@@ -264,6 +267,47 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
                           pack_gqa, dtype, _ptr(workspace), ws_bytes, _stream_handle(stream, q.device))
     _check(st)
     return out, (lse if return_lse else None)
+
+
+def attn_fwd_noalloc(q, k, v, *, out, lse=None, causal: bool = False, scale: Optional[float] = None,
+                     cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: Optional[int] = None,
+                     max_seqlen_k: Optional[int] = None, seqused_k=None, rel_bias=None, num_splits: int = 1,
+                     pack_gqa: int = -1, stream=None):
+    """attn_fwd through attn_fwd_noalloc: no workspace; out (and lse, if wanted) are given by
+    the caller, so neither this wrapper nor the library allocates. Returns (out, lse)."""
+    lib = load()
+    varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
+    if varlen:
+        _require(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, "varlen q, k, v must be [total, heads, dim]")
+        Sq, Hq, D = q.shape
+        Sk, Hkv, _ = k.shape
+        B = (cu_seqlens_q if cu_seqlens_q is not None else cu_seqlens_k).numel() - 1
+        _require(max_seqlen_q is not None and max_seqlen_k is not None, "varlen needs max_seqlen_q and max_seqlen_k")
+        out_shape, lse_shape = (Sq, Hq, v.shape[-1]), (Hq, Sq)
+    else:
+        _require(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "dense q, k, v must be [B, S, heads, dim]")
+        B, Sq, Hq, D = q.shape
+        _, Sk, Hkv, _ = k.shape
+        max_seqlen_q = max_seqlen_q or 0
+        max_seqlen_k = max_seqlen_k or 0
+        out_shape, lse_shape = (B, Sq, Hq, v.shape[-1]), (B, Hq, Sq)
+    Dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("rel_bias", rel_bias)):
+        _require(t is None or t.is_contiguous(), f"{name} must be contiguous")
+    if k.dtype != q.dtype or v.dtype != q.dtype or (rel_bias is not None and rel_bias.dtype != q.dtype):
+        raise AttnError(CODE["ATTN_ERR_BAD_DTYPE"], "q, k, v and rel_bias must share one dtype")
+    _require(out is not None, "attn_fwd_noalloc needs a caller-given out")
+    _check_tensors(q, k, v, varlen=varlen, B=B, Sq=Sq, Hq=Hq, D=D, cu_seqlens_q=cu_seqlens_q,
+                   cu_seqlens_k=cu_seqlens_k, seqused_k=seqused_k, rel_bias=rel_bias, rel_r=None,
+                   rel_proj=None, out=out, lse=lse, workspace=None, out_shape=out_shape, lse_shape=lse_shape)
+    E = 0 if rel_bias is None else int(rel_bias.shape[-1])
+    st = lib.attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, Dv,
+                              float(1.0 / math.sqrt(D) if scale is None else scale), int(bool(causal)),
+                              _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), max_seqlen_q, max_seqlen_k, _ptr(seqused_k),
+                              _ptr(rel_bias), E, num_splits, pack_gqa, _dtype_code(q),
+                              _stream_handle(stream, q.device))
+    _check(st)
+    return out, lse
 
 
 def attn_combine(o_partial, lse_partial, *, out, lse=None, B: int, Sq: int, is_varlen: bool = False,

@@ -425,6 +425,7 @@ const char* attn_status_string(attn_status_t s) {
         case ATTN_ERR_BAD_SPLITS: return "num_splits must be in [1, 256]";
         case ATTN_ERR_BAD_SCALE: return "scale must be finite";
         case ATTN_ERR_BAD_ARG: return "pack_gqa must be -1, 0 or 1";
+        case ATTN_ERR_SCRATCH: return "the split partials exceed the library's 16 MiB array (attn_fwd_noalloc)";
     }
     return "unknown status";
 }

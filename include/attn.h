@@ -60,12 +60,16 @@ typedef enum {
     ATTN_ERR_HIP = 11,              /* the HIP runtime reported an error at launch */
     ATTN_ERR_BAD_SPLITS = 12,       /* attn_combine: num_splits outside [1, ATTN_MAX_SPLITS] */
     ATTN_ERR_BAD_SCALE = 13,        /* scale is NaN or infinite */
-    ATTN_ERR_BAD_ARG = 14           /* pack_gqa not in {-1, 0, 1} */
+    ATTN_ERR_BAD_ARG = 14,          /* pack_gqa not in {-1, 0, 1} */
+    ATTN_ERR_SCRATCH = 15           /* attn_fwd_noalloc: the split partials exceed ATTN_SCRATCH_BYTES */
 } attn_status_t;
 
 typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1 } attn_dtype_t;
 
 #define ATTN_MAX_SPLITS 256
+
+/* Bytes of split partials attn_fwd_noalloc can hold (its device-resident array). */
+#define ATTN_SCRATCH_BYTES (16u << 20)
 
 /*
  * attn_fwd -- the fused attention forward (dense or varlen, optional split-KV).
@@ -147,6 +151,27 @@ attn_status_t attn_fwd_rel_proj(const void* q, const void* k, const void* v, voi
                                 const void* rel_r, const void* rel_proj, int d_rel, int rel_extent,
                                 int num_splits, int pack_gqa, attn_dtype_t dtype, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_noalloc -- attn_fwd for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments minus the workspace. When the key range is split, the partials go to an
+ * array of ATTN_SCRATCH_BYTES (16 MiB) that the library holds in device memory on
+ * every GPU it runs on, until the process ends; the call itself allocates and frees
+ * nothing. Needs ns * rows_q * Hq * (Dv + 1) * 4 <= ATTN_SCRATCH_BYTES bytes for the
+ * split count ns that attn_num_splits gives (rows_q = B * Sq dense, total_q varlen),
+ * else returns ATTN_ERR_SCRATCH and launches nothing (pass a smaller num_splits, or use
+ * attn_fwd with a workspace). Calls on one GPU share that array: calls that overlap in
+ * time on the same GPU (other streams, other threads) must not be made. Results,
+ * errors and ownership otherwise as attn_fwd (it is attn_fwd with that array as the
+ * workspace).
+ */
+attn_status_t attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                               int B, int Sq, int Sk, int Hq, int Hkv, int D, int Dv, float scale,
+                               int causal, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                               int max_seqlen_q, int max_seqlen_k, const int* seqused_k,
+                               const void* rel_bias, int rel_extent, int num_splits, int pack_gqa,
+                               attn_dtype_t dtype, void* stream);
 
 /*
  * attn_check_args -- attn_fwd's validation alone, on the host, with no GPU work

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert "gfx950" in fa.version()
-    for code in range(0, 15):
+    for code in range(0, 16):
         s = fa.status_string(code)
         assert s and s != "unknown status"
     assert fa.status_string(99) == "unknown status"
@@ -227,6 +227,37 @@ def test_tile_bytes_bound_per_class(lib, D, hkv_max):
     assert check(lib, B=1, Sq=1, Sk=1, Hq=over, Hkv=over, D=D, Dv=D) == CODE["ATTN_ERR_BAD_SHAPE"]
     # the larger of D and Dv decides
     assert check(lib, B=1, Sq=1, Sk=1, Hq=over, Hkv=over, D=8, Dv=D) == CODE["ATTN_ERR_BAD_SHAPE"]
+
+
+def noalloc(lib, **over):
+    """attn_fwd_noalloc with arguments it rejects before any HIP call: no GPU call."""
+    a = args(**over)
+    return lib.attn_fwd_noalloc(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Sq"], a["Sk"], a["Hq"],
+                                a["Hkv"], a["D"], a["Dv"], a["scale"], a["causal"], a["cu_q"], a["cu_k"],
+                                a["max_q"], a["max_k"], a["seqused"], a["bias"], a["E"], a["ns"], a["pack"],
+                                a["dtype"], None)
+
+
+def test_noalloc_rejections(lib):
+    # attn_fwd's own errors, in attn_fwd's order
+    assert noalloc(lib, dtype=7) == CODE["ATTN_ERR_BAD_DTYPE"]
+    assert noalloc(lib, Dv=100) == CODE["ATTN_ERR_UNSUPPORTED_HEAD_DIM"]
+    assert noalloc(lib, q=None) == CODE["ATTN_ERR_NULL_POINTER"]
+    assert noalloc(lib, out=A + 8, ns=4) == CODE["ATTN_ERR_MISALIGNED"]
+    assert noalloc(lib, pack=3) == CODE["ATTN_ERR_BAD_ARG"]
+    # partials beyond the 16 MiB array: the largest split count that fits (256 rows x 16
+    # heads x 129 floats per split), and one more that does not
+    rows, per = 256 * 16, 129 * 4
+    fit = fa.SCRATCH_BYTES // (rows * per)
+    assert fit == 7
+    assert fa.workspace_size(1, 256, 16, 128, splits=fit) <= fa.SCRATCH_BYTES
+    assert fa.workspace_size(1, 256, 16, 128, splits=fit + 1) > fa.SCRATCH_BYTES
+    assert noalloc(lib, Sq=256, Sk=65536, Hq=16, Hkv=16, ns=fit + 1) == CODE["ATTN_ERR_SCRATCH"]
+    assert noalloc(lib, Sq=256, Sk=65536, Hq=16, Hkv=16, ns=64) == CODE["ATTN_ERR_SCRATCH"]
+    # the heuristic's own choice counts: 64 rows x 8 heads over 2^20 keys split 256 ways
+    ns = fa.num_splits(1, 64, 1 << 20, 8, 8, 128, 128)
+    assert fa.workspace_size(1, 64, 8, 128, splits=ns) > fa.SCRATCH_BYTES
+    assert noalloc(lib, Sq=64, Sk=1 << 20, ns=0) == CODE["ATTN_ERR_SCRATCH"]
 
 
 def combine(lib, o=A, l=A, ns=2, out=A, lse=A, B=1, Sq=16, Hq=8, Dv=128, varlen=0, dtype=0):
