@@ -8,7 +8,8 @@ already resident in HBM. The default workload is the non-causal MHA forward
 q/k/v [1, 20480, 56, 128] in bf16 (video joint-attention shape).
 
 Reported:
-  value       whole-job TFLOP/s (GB/s for the decode workload) over the K timed steps
+  value       whole-job TFLOP/s (GB/s when the workload is HBM-bound: decode, short-query
+              cached prediction) over the K timed steps
   roofline    achieved / peak of the dominant kernel: algorithmic FLOPs (or bytes) per
               launch / its mean duration from HIP events on the launch stream;
               traffic = HBM bytes per launch from FETCH_SIZE / WRITE_SIZE counters
@@ -16,6 +17,8 @@ Reported:
   cpu_baseline the fp64 CPU oracle timed on a bounded sample of rows of the same
               workload, scaled to the same unit
   check       GPU vs oracle on those sampled rows
+  decode      (after a prefill workload) the decode workload c5b timed in the same run:
+              GB/s over its own timed calls, kernel_ms from HIP events, HBM fraction
 
 Algorithmic work: 2*D + 2*Dv FLOPs per visible (query row, key, head) triple (2*D for
 QK^T, 2*Dv for PV); masked, padded and skipped pairs count nothing. Decode bytes: every valid
@@ -54,6 +57,9 @@ DESCRIPTION = {
     "n1a": "cached prediction fp16 MQA 8:1 D64, q[1,16,8,64] k/v[1,300000,1,64], split-KV",
     "n1b": "cached prediction fp16 MQA 8:1 D64, q[1,64,8,64] k/v[1,300000,1,64], split-KV",
     "n1c": "cached prediction fp16 MQA 8:1 D64, q[1,256,8,64] k/v[1,300000,1,64], split-KV",
+    "n2a": "non-causal MHA bf16 [2,8192,32,48] (head dim 48, on the class-64 kernel)",
+    "n2b": "non-causal MHA bf16 [2,8192,32,72] (head dim 72, on the class-128 kernel)",
+    "n2c": "non-causal MHA bf16 [2,8192,32,128] (head dim 128, for comparison)",
 }
 
 
@@ -91,6 +97,10 @@ def algorithmic_bytes(spec, x):
     kv = int(kl.sum()) * spec.Hkv * (spec.D + spec.Dv) * 2
     rows = int(ql.sum()) * spec.Hq
     return kv + rows * (spec.D * 2 + spec.Dv * 2 + 4)
+
+
+def hbm_bound(spec, x):
+    return algorithmic_flops(spec, x) < algorithmic_bytes(spec, x) * (PEAK_MFMA_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
 
 
 def kernel_source_hash():
@@ -182,6 +192,144 @@ def write_traffic(args, fetch_dir, write_dir):
     print(open(path).read())
 
 
+# SQ counter passes (one rocprofv3 --pmc run each: at most 8 SQ and 2 GRBM counters a pass)
+COUNTER_PASSES = (
+    "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_SALU SQ_INSTS_VMEM "
+    "SQ_WAVES GRBM_GUI_ACTIVE",
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAVE_CYCLES "
+    "SQ_WAIT_INST_ANY SQ_ACTIVE_INST_LDS SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+)
+
+
+def _csv_rows(run_dir, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*" + suffix), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one *{suffix} under {run_dir}, found {files}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _simd_count(run_dir):
+    for r in _csv_rows(run_dir, "agent_info.csv"):
+        if r.get("Agent_Type") == "GPU":
+            return int(r["Simd_Count"])
+    return 1024
+
+
+def pass_counters(run_dir):
+    """Counter means over the forward-kernel dispatches of one --pmc run (the first, cold
+    dispatch left out), plus each dispatch's duration."""
+    per = {}
+    for r in _csv_rows(run_dir, "counter_collection.csv"):
+        if "attn_fwd_kernel" not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(int(r["Dispatch_Id"]), {"_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(per)[1:] or sorted(per)
+    if not ids:
+        raise SystemExit(f"{run_dir}: no forward-kernel dispatch")
+    names = {n for i in ids for n in per[i]}
+    return {n: float(np.mean([per[i].get(n, 0.0) for i in ids])) for n in names}, len(ids)
+
+
+def kernel_stats(trace_dir):
+    rows = _csv_rows(trace_dir, "kernel_stats.csv")
+    return [(r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+             float(r["MaxNs"]) / 1e3) for r in rows]
+
+
+def timed_forward_us(trace_dir, steps):
+    """Durations of the last `steps` forward-kernel dispatches (the timed calls) in us."""
+    rows = _csv_rows(trace_dir, "kernel_trace.csv")
+    fwd = sorted((int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+                 for r in rows if "attn_fwd_kernel" in r["Kernel_Name"])
+    return [d for _, d in fwd[-steps:]]
+
+
+def write_summary(args):
+    """profiles/attn_fwd_d<class>_<dtype>_<workload>.md from a kernel-trace run and the SQ
+    counter passes of COUNTER_PASSES (no GPU run)."""
+    from workloads import configs
+    spec = configs.workload(args.workload, args.dtype)
+    x = configs.make_inputs(spec)
+    flops = algorithmic_flops(spec, x)
+    nbytes = algorithmic_bytes(spec, x)
+    trace_dir, pmc_dirs = args.summarize[0], args.summarize[1:]
+    dclass = next(c for c in (16, 64, 128, 256) if max(spec.D, spec.Dv) <= c)
+    name = f"attn_fwd_d{dclass}_{spec.dtype}_{args.workload}"
+    wl = f"--workload {args.workload} --dtype {spec.dtype}"
+    lines = [f"# {name}: {DESCRIPTION[args.workload]}", ""]
+    lines += ["Commands, from the repository root with TMPDIR=/tmp (rocprofv3 writes CSV under -d):", "", "```"]
+    lines.append(f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o run -- "
+                 f"python3 -u bench.py --no-cpu --decode-steps 0 --steps {args.steps} --warmup 3 {wl}")
+    for i, d in enumerate(pmc_dirs):
+        lines.append(f"rocprofv3 --pmc {COUNTER_PASSES[i]} --output-format csv -d {d} -o run -- "
+                     f"python3 -u bench.py --no-cpu --decode-steps 0 --steps 3 --warmup 1 --warmup-seconds 0 {wl}")
+    lines.append(f"python3 bench.py {wl} --steps {args.steps} --summarize {trace_dir} {' '.join(pmc_dirs)}")
+    lines += ["```", ""]
+    lines += ["Kernel statistics over every dispatch of the trace run (the first call, warm-up and "
+              "timed calls):", "", "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for n, c, a, mn, mx in kernel_stats(trace_dir):
+        lines.append(f"| `{n[:110]}` | {c} | {a:.1f} | {mn:.1f} | {mx:.1f} |")
+    t = timed_forward_us(trace_dir, args.steps)
+    fwd_us = float(np.mean(t))
+    lines += ["", f"The {len(t)} timed forward dispatches: mean {fwd_us:.1f} us (min {min(t):.1f}, max {max(t):.1f}).",
+              f"Algorithmic work per call: {flops:.4g} FLOP (2*D + 2*Dv per visible (row, key, head)), "
+              f"{nbytes:.4g} bytes (K and V of every valid key once, plus q, O, LSE).",
+              f"Forward kernel alone: {flops / (fwd_us * 1e-6) / 1e12:.1f} TFLOP/s = "
+              f"{flops / (fwd_us * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS:.3f} of {PEAK_MFMA_TFLOPS:.0f} TFLOP/s; "
+              f"{nbytes / (fwd_us * 1e-6) / 1e9:.0f} GB/s = {nbytes / (fwd_us * 1e-6) / 1e9 / PEAK_HBM_GBS:.3f} "
+              f"of {PEAK_HBM_GBS:.0f} GB/s."]
+    if pmc_dirs:
+        simd = _simd_count(pmc_dirs[0])
+        merged, derived = {}, {}
+        for d in pmc_dirs:
+            c, n = pass_counters(d)
+            gui = c["GRBM_GUI_ACTIVE"] / 8.0  # summed over the 8 XCDs, which run in lockstep
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                derived["mfma_busy"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * simd)
+                derived["lds_wait"] = c["SQ_WAIT_INST_LDS"] / c["SQ_WAVE_CYCLES"]
+                derived["any_wait"] = c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]
+                derived["clock"] = gui / c["_ns"]
+            for kname, val in c.items():
+                if kname != "_ns" and kname != "GRBM_GUI_ACTIVE":
+                    merged[kname] = val
+            merged.setdefault("GRBM_GUI_ACTIVE (per XCD)", gui)
+        if "SQ_INSTS_MFMA" in merged and merged["SQ_INSTS_MFMA"] > 0:
+            derived["valu_per_mfma"] = (merged["SQ_INSTS_VALU"] - merged["SQ_INSTS_MFMA"]) / merged["SQ_INSTS_MFMA"]
+        elif "SQ_INSTS_VALU" in merged:
+            derived["valu_per_mfma"] = float("inf")
+        lines += ["", f"SQ counters per forward dispatch (mean over the dispatches after the first; {simd} SIMDs):",
+                  "", "| counter | value |", "|---|---|"]
+        for kname in sorted(merged):
+            lines.append(f"| {kname} | {merged[kname]:.4g} |")
+        lines += ["", "Derived:", ""]
+        if "mfma_busy" in derived:
+            lines.append(f"- MFMA busy: {derived['mfma_busy']:.3f} = SQ_VALU_MFMA_BUSY_CYCLES / "
+                         f"(GRBM_GUI_ACTIVE / 8 x {simd} SIMDs)")
+            lines.append(f"- LDS-wait share: {derived['lds_wait']:.3f} = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES "
+                         f"(any wait: {derived['any_wait']:.3f} = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)")
+            lines.append(f"- shader clock while counting: {derived['clock']:.2f} GHz = GRBM_GUI_ACTIVE / 8 / "
+                         f"dispatch duration")
+        if "valu_per_mfma" in derived:
+            lines.append(f"- VALU per MFMA: {derived['valu_per_mfma']:.2f} = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / "
+                         f"SQ_INSTS_MFMA")
+        if "SQ_INSTS_VALU_TRANS_F32" in merged and merged.get("SQ_INSTS_VALU"):
+            lines.append(f"- transcendental share of VALU: "
+                         f"{merged['SQ_INSTS_VALU_TRANS_F32'] / merged['SQ_INSTS_VALU']:.3f}")
+    tr = read_traffic(args.workload, spec.dtype)
+    lines += ["", (f"HBM traffic per forward launch (FETCH_SIZE + WRITE_SIZE, calibrated): {tr:.4g} bytes "
+                   f"(profiles/traffic_{args.workload}_{spec.dtype}.txt)") if tr is not None else
+              "HBM traffic: not taken on these kernel sources."]
+    lines += ["", f"Kernel sources hash {kernel_source_hash()}.", ""]
+    path = os.path.join(REPO, "profiles", name + ".md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def graph_timing(fa, q, k, v, kw, steps, eager_ms_step, kernel_ms):
     """Microseconds per call: eager (the timed loop above), one call captured in a HIP
     graph and replayed back to back, and the kernels alone (events)."""
@@ -204,8 +352,33 @@ def graph_timing(fa, q, k, v, kw, steps, eager_ms_step, kernel_ms):
         g.replay()
     torch.cuda.synchronize()
     graph_us = (time.perf_counter() - t0) * 1e6 / steps
+    # the floor of either way of launching: a one-element fill kernel, launched directly
+    # and as a captured one-kernel graph, back to back
+    tiny = torch.zeros(1, device="cuda")
+    n = max(steps, 200)
+
+    def per_call_us(fn):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e6 / n
+
+    eager_fill_us = per_call_us(lambda: tiny.fill_(1.0))
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        tiny.fill_(0.0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g2):
+        tiny.fill_(1.0)
+    torch.cuda.synchronize()
+    graph_fill_us = per_call_us(g2.replay)
     return {"eager_us_per_call": eager_ms_step * 1e3, "graph_us_per_call": graph_us,
-            "kernel_us_per_call": kernel_ms * 1e3}
+            "kernel_us_per_call": kernel_ms * 1e3, "fill_kernel_eager_us_per_call": eager_fill_us,
+            "fill_kernel_graph_us_per_call": graph_fill_us}
 
 
 def sample_rows(spec, x, n, seed=12345):
@@ -273,50 +446,22 @@ def cpu_baseline(spec, x, out, lse, target_s, threads):
             "sample": sample, "seconds": round(dt, 3), "sample_flop": flops}, check
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--warmup-seconds", type=float, default=1.0,
-                    help="keep warming up (untimed steps) until this much time has passed as well: "
-                         "the GPU needs some hundred milliseconds of load to reach its steady clocks, "
-                         "longer than a few steps of a sub-millisecond call")
-    ap.add_argument("--workload", default="c2", choices=sorted(DESCRIPTION))
-    ap.add_argument("--dtype", default=None, choices=["bf16", "fp16"])
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target wall time of the oracle sample")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the call captured in a HIP graph and replayed (host "
-                         "dispatch overhead: eager vs graph microseconds per call)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB elementwise copy (counter calibration)")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="no GPU run: turn the counter CSVs of two rocprofv3 --pmc runs of "
-                         "bench.py --copy-calibration (FETCH_SIZE, then WRITE_SIZE) into "
-                         "profiles/traffic_<workload>_<dtype>.txt")
-    args = ap.parse_args()
-    if args.traffic_from:
-        write_traffic(args, *args.traffic_from)
-        return
-    if args.gpus != 1:
-        print(f"bench.py: measures one GPU only (asked for {args.gpus}); the path would "
-              "shard over (batch, KV head) with no exchange, or over the key range with one "
-              "LSE combine step", file=sys.stderr)
-        sys.exit(2)
+class Run:
+    """One workload's inputs resident in HBM, its preallocated outputs, and its timings."""
 
+
+def time_workload(workload, dtype, steps, warmup, warmup_seconds, copy_calibration=False):
+    """Generate the workload's synthetic inputs, copy them to the GPU, warm up, then time
+    exactly `steps` calls (wall clock around all of them, HIP events around each one on
+    the launch stream)."""
     import torch
 
     import exact_attention_forward_amd as fa
     from workloads import configs
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    fa.load()
-    spec = configs.workload(args.workload, args.dtype)
-    log(f"generating {args.workload} ({DESCRIPTION[args.workload]}) {spec.dtype}")
+    r = Run()
+    spec = configs.workload(workload, dtype)
+    log(f"generating {workload} ({DESCRIPTION[workload]}) {spec.dtype}")
     x = configs.make_inputs(spec)
     tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[spec.dtype]
 
@@ -351,17 +496,18 @@ def main():
     kw.update(out=out, lse=lse, workspace=ws)
     torch.cuda.synchronize()
 
-    if args.copy_calibration:
+    if copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.float16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
+        del src, dst
         log("copy calibration: 3 x elementwise copy of 1 GiB")
 
     t_w = time.perf_counter()
     n_warm = 0
-    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
+    while n_warm < warmup or time.perf_counter() - t_w < warmup_seconds:
         fa.attn_fwd(q, k, v, **kw)
         n_warm += 1
         if n_warm % 16 == 0:
@@ -370,7 +516,7 @@ def main():
     log(f"warm-up: {n_warm} untimed steps in {time.perf_counter() - t_w:.2f} s")
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+          for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e0, e1 in ev:
@@ -380,11 +526,85 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_call_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
-    ms_step = wall * 1e3 / args.steps
-    mean_call_ms = float(np.mean(per_call_ms))
+    r.spec, r.x, r.q, r.k, r.v, r.kw, r.out, r.lse = spec, x, q, k, v, kw, out, lse
+    r.varlen, r.ns, r.n_warm = varlen, ns, n_warm
+    r.ms_step = wall * 1e3 / steps
+    r.mean_call_ms = float(np.mean(per_call_ms))
+    return r
+
+
+def decode_summary(r):
+    """The decode sub-object: HBM-bound split-KV forward + combine."""
+    nbytes = algorithmic_bytes(r.spec, r.x)
+    achieved = nbytes / (r.mean_call_ms * 1e-3) / 1e9
+    return {"workload": f"c5b: {DESCRIPTION['c5b']}", "value": nbytes / (r.ms_step * 1e-3) / 1e9,
+            "unit": "GB/s", "ms_per_step": r.ms_step, "kernel_ms": r.mean_call_ms,
+            "achieved": achieved, "peak": PEAK_HBM_GBS, "frac": achieved / PEAK_HBM_GBS,
+            "algorithmic_bytes": nbytes, "num_splits": r.ns, "kernels_per_launch": 2 if r.ns > 1 else 1,
+            "dtype": r.spec.dtype}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="keep warming up (untimed steps) until this much time has passed as well: "
+                         "the GPU needs some hundred milliseconds of load to reach its steady clocks, "
+                         "longer than a few steps of a sub-millisecond call")
+    ap.add_argument("--workload", default="c2", choices=sorted(DESCRIPTION))
+    ap.add_argument("--dtype", default=None, choices=["bf16", "fp16"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
+    ap.add_argument("--decode-steps", type=int, default=100,
+                    help="timed calls of the decode workload (c5b) reported in the line's 'decode' "
+                         "object after a prefill workload; 0 skips it (profiling runs)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the call captured in a HIP graph and replayed (host "
+                         "dispatch overhead: eager vs graph microseconds per call)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB elementwise copy (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: turn the counter CSVs of two rocprofv3 --pmc runs of "
+                         "bench.py --copy-calibration (FETCH_SIZE, then WRITE_SIZE) into "
+                         "profiles/traffic_<workload>_<dtype>.txt")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="no GPU run: write profiles/attn_fwd_d<class>_<dtype>_<workload>.md from a "
+                         "rocprofv3 --kernel-trace --stats run (first DIR) and --pmc runs of the "
+                         "counter passes in order (further DIRs); --steps = the trace run's timed calls")
+    args = ap.parse_args()
+    if args.summarize:
+        write_summary(args)
+        return
+    if args.traffic_from:
+        write_traffic(args, *args.traffic_from)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: measures one GPU only (asked for {args.gpus}); the path would "
+              "shard over (batch, KV head) with no exchange, or over the key range with one "
+              "LSE combine step", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_forward_amd as fa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    fa.load()
+    r = time_workload(args.workload, args.dtype, args.steps, args.warmup, args.warmup_seconds,
+                      args.copy_calibration)
+    spec, x, q, k, v, kw, out, lse = r.spec, r.x, r.q, r.k, r.v, r.kw, r.out, r.lse
+    varlen, ns, n_warm, ms_step, mean_call_ms = r.varlen, r.ns, r.n_warm, r.ms_step, r.mean_call_ms
 
     flops = algorithmic_flops(spec, x)
-    decode = args.workload in DECODE
+    # the bound follows the arithmetic intensity: below the machine balance (MFMA peak /
+    # HBM peak, about 312 FLOP per byte) the algorithmic bytes cannot arrive faster than HBM
+    # delivers them (decode, the short-query cached prediction), above it the MFMAs bound
+    decode = args.workload in DECODE or hbm_bound(spec, x)
     if decode:
         nbytes = algorithmic_bytes(spec, x)
         value = nbytes / (ms_step * 1e-3) / 1e9
@@ -427,6 +647,15 @@ def main():
             cb["unit"] = "GB/s"
         result["cpu_baseline"] = cb
         result["check"] = check
+    if args.workload not in DECODE and args.decode_steps > 0:
+        # the metric's decode half, measured in the same run on its own inputs
+        del r, q, k, v, kw, out, lse, x
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        rd = time_workload(DECODE[0], None, args.decode_steps, args.warmup, args.warmup_seconds)
+        result["decode"] = decode_summary(rd)
+        log(f"decode {DECODE[0]}: {rd.ms_step:.4f} ms/step wall, {rd.mean_call_ms:.4f} ms/call events, "
+            f"{result['decode']['frac']:.3f} of HBM peak")
     print(json.dumps(result), flush=True)
 
 

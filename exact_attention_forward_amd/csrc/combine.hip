@@ -33,16 +33,23 @@ __device__ __forceinline__ uint16_t narrow(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
-// One work-group of 4 waves per (query row, head). The split-wise max and sum
-// run over all 256 threads; then wave w accumulates the splits s = w, w+4, ...
-// with its lanes over the Dv columns (several partial rows in flight per lane),
-// and the four partial sums meet in LDS.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One work-group of 256 threads per (query row, head). Thread s holds split s's LSE
+// (num_splits <= 256): the max, the sum and the weights exp(LSE_s - LSE) come from one
+// read each, and the weights go to LDS. Then the threads take 16-byte column chunks of
+// the partial rows, SP splits side by side (thread = split slot x chunk), each with
+// UNROLL rows in flight, and the SP partial sums of a chunk meet in LDS in a fixed order.
+// Splits with weight 0 (empty key ranges) are skipped, whatever their partial holds.
 template <int DV, bool BF>
 __global__ void __launch_bounds__(256) attn_combine_kernel(const CombineParams p) {
-    constexpr int PER = DV >= 64 ? DV / 64 : 1;  // columns per lane
-    constexpr int UNROLL = 16 / PER;              // splits per wave in flight (16 loads per lane)
+    constexpr int CH = DV / 4;     // 16-byte chunks of a row
+    constexpr int SP = 256 / CH;   // splits read side by side
+    constexpr int UNROLL = 8;      // partial rows in flight per thread
+    static_assert(CH * SP == 256, "a row's chunks tile the work-group");
     __shared__ float red[4];
-    __shared__ float part[4][DV];
+    __shared__ float wts[256];
+    __shared__ f32x4 part[SP][CH];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -58,71 +65,56 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const CombineParams p
         lidx = (bb * p.Hq + h) * p.Sq + i;
     }
     const long long lse_stride = p.rows_q * p.Hq;  // per split
-    const float* lp = p.lse_part + lidx;
+    const float ls = tid < p.ns ? p.lse_part[lidx + (long long)tid * lse_stride] : -INFINITY;
 
-    // M = max_s LSE_s over the work-group
-    float M = -INFINITY;
-    for (int s = tid; s < p.ns; s += 256) M = fmaxf(M, lp[(long long)s * lse_stride]);
-    M = wave_max(M);
+    // M = max_s LSE_s, LSE = M + ln sum_s exp(LSE_s - M)
+    float M = wave_max(ls);
     if (lane == 0) red[wave] = M;
     __syncthreads();
     M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
-
     float L = -INFINITY;
     if (M != -INFINITY) {  // uniform over the work-group
-        float sum = 0.f;
-        for (int s = tid; s < p.ns; s += 256) sum += expf(lp[(long long)s * lse_stride] - M);
-        sum = wave_sum(sum);
-        if (lane == 0) red[wave] = sum;
+        const float e = wave_sum(expf(ls - M));  // exp(-inf) = 0 past the last split
+        if (lane == 0) red[wave] = e;
         __syncthreads();
         L = M + logf((red[0] + red[1]) + (red[2] + red[3]));
     }
+    wts[tid] = expf(ls - L);  // (unused when L = -inf)
+    __syncthreads();
 
-    const int dv0 = lane * PER;
-    const bool active = dv0 < p.Dv;  // Dv <= DV, a multiple of 8 (whole PER-column groups)
-    float acc[PER];
-#pragma unroll
-    for (int e = 0; e < PER; e++) acc[e] = 0.f;
+    const int c = tid % CH, sg = tid / CH;
+    const bool active = 4 * c < p.Dv;  // Dv <= DV, a multiple of 8: whole chunks
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (L != -INFINITY && active) {
-        const float* op = p.o_part + item * p.Dv + dv0;
+        const float* op = p.o_part + item * p.Dv + 4 * c;
         const long long ostride = lse_stride * p.Dv;  // floats between splits
-        int s = wave;
-        for (; s + 4 * (UNROLL - 1) < p.ns; s += 4 * UNROLL) {
-            float w[UNROLL], x[UNROLL][PER];
+        int s = sg;
+        for (; s + SP * (UNROLL - 1) < p.ns; s += SP * UNROLL) {
+            f32x4 x[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; u++) x[u] = *(const f32x4*)(op + (long long)(s + SP * u) * ostride);
 #pragma unroll
             for (int u = 0; u < UNROLL; u++) {
-                const long long su = s + 4 * u;
-                w[u] = lp[su * lse_stride];
-#pragma unroll
-                for (int e = 0; e < PER; e++) x[u][e] = op[su * ostride + e];
-            }
-#pragma unroll
-            for (int u = 0; u < UNROLL; u++) {
-                const float wu = expf(w[u] - L);  // 0 for an empty split (LSE_s = -inf)
-                if (wu != 0.f)
-#pragma unroll
-                    for (int e = 0; e < PER; e++) acc[e] += wu * x[u][e];
+                const float w = wts[s + SP * u];
+                if (w != 0.f) acc += w * x[u];
             }
         }
-        for (; s < p.ns; s += 4) {
-            const float wu = expf(lp[(long long)s * lse_stride] - L);
-            if (wu != 0.f)
-#pragma unroll
-                for (int e = 0; e < PER; e++) acc[e] += wu * op[(long long)s * ostride + e];
+        for (; s < p.ns; s += SP) {
+            const float w = wts[s];
+            if (w != 0.f) acc += w * *(const f32x4*)(op + (long long)s * ostride);
         }
     }
-    if (active)
-#pragma unroll
-        for (int e = 0; e < PER; e++) part[wave][dv0 + e] = acc[e];
+    part[sg][c] = acc;
     __syncthreads();
-    if (wave == 0 && active) {
-        uint16_t* dst = p.out + item * p.Dv + dv0;
+    if (tid < CH && active) {
+        f32x4 o = part[0][tid];
 #pragma unroll
-        for (int e = 0; e < PER; e++) {
-            const int c = dv0 + e;
-            dst[e] = narrow<BF>((part[0][c] + part[1][c]) + (part[2][c] + part[3][c]));
-        }
+        for (int g = 1; g < SP; g++) o += part[g][tid];
+        uint16_t* dst = p.out + item * p.Dv + 4 * tid;
+        const unsigned lo = (unsigned)narrow<BF>(o[0]) | ((unsigned)narrow<BF>(o[1]) << 16);
+        const unsigned hi = (unsigned)narrow<BF>(o[2]) | ((unsigned)narrow<BF>(o[3]) << 16);
+        *(uint2*)dst = make_uint2(lo, hi);
     }
     if (p.lse && tid == 0) p.lse[lidx] = L;
 }

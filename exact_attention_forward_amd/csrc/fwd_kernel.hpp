@@ -44,6 +44,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
 typedef short s16x4v __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) s16x4v lds_s16x4;
 
@@ -547,16 +548,21 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
                 }
         }
     };
-    // From HBM: one buffer read per element, all at one per-lane offset plus an
-    // immediate. Within a lane the d of a tile's elements fall in a window of
-    // CMAX + 1 values below d0, and over the lanes of a band tile d0 >= -35, so
-    // with the descriptor starting one bias row before the wave's first row
-    // (first >= 1) every offset is positive; a read that leaves the tensor returns
-    // 0 (such elements lie outside the band). Otherwise (the wave holds the
-    // tensor's first row, or a wave's rows span more than 2^31 bytes of bias) the
-    // reads take clamped indices.
+    // From HBM. A lane's elements come in groups of four consecutive keys (r = 4g ..
+    // 4g + 3), whose d are four consecutive values of one bias row, highest d first;
+    // each group is one 12-byte read from the dword boundary at or below its lowest d
+    // (all of a lane's groups share that d's parity, so one funnel shift per word pair
+    // puts the four values in place), all at one per-lane offset plus an immediate.
+    // Within a lane the d of a tile's elements fall in a window of CMAX + 1 values
+    // below d0, and over the lanes of a band tile d0 >= -35, so with the descriptor
+    // starting one bias row before the wave's first row (first >= 1) every offset is
+    // positive; a read reaches at most two values past a group, which stay inside the
+    // tensor unless the wave holds its last row (then, as when the wave holds the first
+    // row or its rows span more than 2^31 bytes of bias, the reads take clamped
+    // indices). Values outside the band are masked whatever they hold.
     auto load_bias_global = [&](BiasBits& bb, int j0, long long base_row) __attribute__((always_inline)) {
         constexpr int CMAX = (T::NKB - 1) * 32 + 27;  // largest key offset within the tile, less 4hf
+        constexpr int CG = CMAX - 3;                  // offset of the last group's first key
         const char* base = (const char*)p.bias + base_row * p.E * 2;
         const long long left = ((long long)p.rows_q * p.Hq - base_row) * p.E * 2;
         const int nrec = __builtin_amdgcn_readfirstlane((int)min(left, (long long)INT32_MAX));
@@ -574,32 +580,44 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             const int d0 = i + delta - j0 - 4 * hf;  // d of element (kb2, r) is d0 - c(kb2, r)
             // in the band (0 <= d < E, valid row) iff blo <= c <= bhi
             const int bhi = qvalid[qb] ? d0 : -1, blo = d0 - p.E + 1;
+            // byte offset of d0 - CMAX, the lowest d of the last group; group (kb2, g) starts
+            // 2 (CG - c_g) bytes above it, c_g = 32 kb2 + 8 g (a multiple of 16 bytes)
             const int vo = (int)((row - base_row) * p.E + d0 - CMAX) * 2;
-            uint32_t raw[T::NKB][16];
+            const int v4 = vo & ~3;
+            const int sh = (vo & 2) * 8;  // 16: the group's lowest d is the upper half of a word
+            u32x3 raw[T::NKB][4];
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int c = kb2 * 32 + 8 * (r >> 2) + (r & 3);
-                    raw[kb2][r] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, vo + 2 * (CMAX - c), 0, 0);
-                }
+                for (int g = 0; g < 4; g++)
+                    raw[kb2][g] = __builtin_bit_cast(
+                        u32x3, __builtin_amdgcn_raw_buffer_load_b96(rsrc, v4 + 2 * (CG - kb2 * 32 - 8 * g), 0, 0));
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
-                for (int r2 = 0; r2 < 8; r2++) {
-                    uint32_t w = 0;
+                for (int g = 0; g < 4; g++) {
+                    // the group's four values in ascending d: (a0, a1) in w_lo, (a2, a3) in w_hi;
+                    // element e = r & 3 has d = d0 - c_g - e, i.e. value a(3 - e)
+                    const u32x3 x = raw[kb2][g];
+                    const uint32_t w_lo = __builtin_amdgcn_alignbit(x[1], x[0], sh);
+                    const uint32_t w_hi = __builtin_amdgcn_alignbit(x[2], x[1], sh);
+                    const uint32_t pr[2] = {__builtin_amdgcn_alignbit(w_hi, w_hi, 16),   // elements 4g, 4g + 1
+                                            __builtin_amdgcn_alignbit(w_lo, w_lo, 16)};  // elements 4g + 2, 4g + 3
 #pragma unroll
-                    for (int e = 0; e < 2; e++) {
-                        const int r = 2 * r2 + e;
-                        const int c = kb2 * 32 + 8 * (r >> 2) + (r & 3);
-                        const bool vis = lim_vis(lim, qb, kb2, r);
-                        const bool keep = vis && c <= bhi && c >= blo;
-                        // masked: the -inf of the dtype; visible outside the band: 0
-                        const uint32_t h = (raw[kb2][r] & (keep ? 0xFFFFu : 0u)) |
-                                           (vis ? 0u : (uint32_t)E::kNegInfBits);
-                        w |= h << (16 * e);
+                    for (int h2 = 0; h2 < 2; h2++) {
+                        uint32_t keepm = 0, neg = 0;
+#pragma unroll
+                        for (int e = 0; e < 2; e++) {
+                            const int r = 4 * g + 2 * h2 + e;
+                            const int c = kb2 * 32 + 8 * g + 2 * h2 + e;
+                            const bool vis = lim_vis(lim, qb, kb2, r);
+                            const bool keep = vis && c <= bhi && c >= blo;
+                            // masked: the -inf of the dtype; visible outside the band: 0
+                            keepm |= (keep ? 0xFFFFu : 0u) << (16 * e);
+                            neg |= (vis ? 0u : (uint32_t)E::kNegInfBits) << (16 * e);
+                        }
+                        bb[qb][kb2][2 * g + h2] = (pr[h2] & keepm) | neg;
                     }
-                    bb[qb][kb2][r2] = w;
                 }
         }
     };
@@ -607,6 +625,10 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
     long long bias_first_row = (q_off + min(w_row, r_last) / gp) * p.Hq + h_base;
     bias_first_row = (long long)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)bias_first_row >> 32)) << 32) |
                                  __builtin_amdgcn_readfirstlane((uint32_t)bias_first_row));
+    // and its last (an upper bound: the wave's last query, its last packed head)
+    long long bias_last_row = (q_off + wi_hi) * p.Hq + h_base + gp - 1;
+    bias_last_row = (long long)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)bias_last_row >> 32)) << 32) |
+                                __builtin_amdgcn_readfirstlane((uint32_t)bias_last_row));
     // Fused producer (tml-fa4 page: rel_bias = r . rel_proj, the einsum over d_rel), per
     // band tile, wave and 32-row block. Over the block's rows the tile needs d in
     // [dbase, dbase + BN + 31) with dbase = (block's first query) + delta - j0 - (BN - 1);
@@ -702,8 +724,8 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
     auto load_bias = [&](BiasBits& bb, int j0) __attribute__((always_inline)) {
         if (fused_bias)
             produce_bias(bb, j0);
-        else if (bias_first_row >= 1 && p.E > (T::NKB - 1) * 32 + 27 + 35 &&
-                 (long long)(T::BM + 2) * p.Hq * p.E * 2 < INT32_MAX)
+        else if (bias_first_row >= 1 && bias_last_row + 1 < p.rows_q * p.Hq &&
+                 p.E > (T::NKB - 1) * 32 + 27 + 35 && (long long)(T::BM + 2) * p.Hq * p.E * 2 < INT32_MAX)
             load_bias_global(bb, j0, bias_first_row - 1);  // (offsets fit 31 bits)
         else
             load_bias_from(bb, j0, [&](int qb) { return bias_row(qb); });

@@ -124,6 +124,7 @@ def workload(name: str, dtype: Optional[str] = None) -> Spec:
     c5b  bf16 D256 decode q[32,1,8,256], k/v[32,131072,1,256], causal, split-KV + combine
     n1a/b/c  fp16 cached prediction: q[1,R,8,64] against k/v[1,300000,1,64] (MQA 8:1),
              R = 16 / 64 / 256 query rows, non-causal, split-KV heuristic
+    n2a/b/c  bf16 non-causal MHA [2,8192,32,D] with D = 48 / 72 / 128 (the D48/D72/D128 family)
     """
     s128 = f32(1.0 / math.sqrt(128.0))
     if name == "c1":
@@ -149,15 +150,24 @@ def workload(name: str, dtype: Optional[str] = None) -> Spec:
     if name == "c5b":
         return Spec(name, dtype or gen.BF16, 32, 1, 131072, 8, 1, 256, 256, True, f32(1 / 16), 52,
                     num_splits=0, pack_gqa=1)
+    if name in N2_DIMS:
+        D = N2_DIMS[name]
+        return Spec(name, dtype or gen.BF16, 2, 8192, 8192, 32, 32, D, D, False, f32(1.0 / math.sqrt(D)),
+                    N2_SEEDS[name])
     if name in N1_ROWS:
         return Spec(name, dtype or gen.FP16, 1, N1_ROWS[name], 300000, 8, 1, 64, 64, False, f32(1 / 8),
                     N1_SEEDS[name], num_splits=0)
     raise KeyError(name)
 
 
+# head dims of the D48 / D72 / D128 family on one prefill shape, and seeds
+N2_DIMS = {"n2a": 48, "n2b": 72, "n2c": 128}
+N2_SEEDS = {"n2a": 71, "n2b": 72, "n2c": 73}
+
 # short-query cached prediction: query rows per call and seeds
 N1_ROWS = {"n1a": 16, "n1b": 64, "n1c": 256}
 N1_SEEDS = {"n1a": 61, "n1b": 62, "n1c": 63}
 
-WORKLOADS = ("c1", "c2", "c3", "c3r", "c4a", "c4b", "c4c", "c5a", "c5b", "n1a", "n1b", "n1c")
+WORKLOADS = ("c1", "c2", "c3", "c3r", "c4a", "c4b", "c4c", "c5a", "c5b", "n1a", "n1b", "n1c", "n2a", "n2b",
+             "n2c")
 
