@@ -172,7 +172,7 @@ def write_traffic(args, fetch_dir, write_dir):
     fetch = float(np.mean(f_fwd)) * f_scale
     write = float(np.mean(w_fwd)) * w_scale
     path = os.path.join(REPO, "profiles", f"traffic_{args.workload}_{spec.dtype}.txt")
-    cmd = (f"python -u bench.py --no-cpu --steps 3 --warmup 1 --workload {args.workload} "
+    cmd = (f"python3 -u bench.py --no-cpu --decode-steps 0 --steps 3 --warmup 1 --workload {args.workload} "
            f"--dtype {spec.dtype} --copy-calibration")
     with open(path, "w") as f:
         f.write(f"# HBM traffic of attn_fwd_kernel per launch, {args.workload} "
@@ -293,6 +293,9 @@ def write_summary(args):
                 derived["lds_wait"] = c["SQ_WAIT_INST_LDS"] / c["SQ_WAVE_CYCLES"]
                 derived["any_wait"] = c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]
                 derived["clock"] = gui / c["_ns"]
+                # SQ_ACTIVE_INST_VALU counts 4-cycle units (summed over waves, which cannot issue
+                # VALU on one SIMD in the same cycle): the share of SIMD cycles issuing VALU
+                derived["valu_active"] = 4.0 * c["SQ_ACTIVE_INST_VALU"] / (gui * simd)
             for kname, val in c.items():
                 if kname != "_ns" and kname != "GRBM_GUI_ACTIVE":
                     merged[kname] = val
@@ -311,6 +314,8 @@ def write_summary(args):
                          f"(GRBM_GUI_ACTIVE / 8 x {simd} SIMDs)")
             lines.append(f"- LDS-wait share: {derived['lds_wait']:.3f} = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES "
                          f"(any wait: {derived['any_wait']:.3f} = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)")
+            lines.append(f"- VALU active: {derived['valu_active']:.3f} = 4 x SQ_ACTIVE_INST_VALU / "
+                         f"(GRBM_GUI_ACTIVE / 8 x {simd} SIMDs) (MFMA issue included)")
             lines.append(f"- shader clock while counting: {derived['clock']:.2f} GHz = GRBM_GUI_ACTIVE / 8 / "
                          f"dispatch duration")
         if "valu_per_mfma" in derived:
