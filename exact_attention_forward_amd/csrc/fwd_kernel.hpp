@@ -450,9 +450,14 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             for (int qb = 0; qb < T::NQB; qb++)
 #pragma unroll
                 for (int dt = 0; dt < ODT; dt++) {
+                    // At class 256 (O in AGPRs, more than 256 registers a wave) the block is
+                    // pinned to AGPRs on both sides of its multiply: without the first pin the
+                    // compiler copied all of O to VGPRs at the top of every key-loop iteration
+                    // for this rare block (c5a -7.5% time with it, 443 -> 328 registers a wave)
                     f32x16 x = o[qb][dt];
+                    if (D == 256) asm volatile("" : "+a"(x));
                     x *= alpha[qb];
-                    if (D == 256) asm volatile("" : "+a"(x));  // (512 registers a wave) one block at a time
+                    if (D == 256) asm volatile("" : "+a"(x));
                     o[qb][dt] = x;
                 }
         }
