@@ -91,3 +91,10 @@ def test_n1_cached_prediction(name):
     rows = np.array([[0, h, i] for h in range(8) for i in range(0, c.Sq, max(1, c.Sq // 16))],
                     dtype=np.int32)
     sampled_check(c, rows=rows)
+
+
+@pytest.mark.parametrize("name", ["n2a", "n2b"])
+def test_n2_head_dims_below_class(name):
+    # head dim 48 on the class-64 kernel, 72 on the class-128 kernel, at the timed size
+    c = make_case(name)
+    sampled_check(c, rows=sample_rows(c, max_pairs=6, per_seq_rows=24, tile=256))
