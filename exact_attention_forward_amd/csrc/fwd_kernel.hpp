@@ -73,6 +73,7 @@ struct Elem<true> {  // bfloat16
     }
     static __device__ __forceinline__ __bf16 to_elem(float x) { return (__bf16)x; }
     static constexpr uint16_t kNegInfBits = 0xFF80;
+    static constexpr uint32_t kOnePairBits = 0x3F803F80u;  // (1, 1)
 };
 
 template <>
@@ -89,6 +90,7 @@ struct Elem<false> {  // IEEE half
     }
     static __device__ __forceinline__ _Float16 to_elem(float x) { return (_Float16)x; }
     static constexpr uint16_t kNegInfBits = 0xFC00;
+    static constexpr uint32_t kOnePairBits = 0x3C003C00u;  // (1, 1)
 };
 
 template <int D, bool CAUSAL = false>
@@ -420,6 +422,17 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
     auto partner_sum = [](float x) __attribute__((always_inline)) {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
         return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    };
+    // Head-dim class 16: columns 16..31 of the one 32-column block of O^T are padding, so
+    // the V^T fragment feeds ones into column 16 and the PV MFMA accumulates there each
+    // row's sum of the rounded weights it multiplies V by: the normaliser takes no VALU
+    // adds, and a rescale of O rescales it too. Lane half 0 holds column 16 (o[qb][0][8]);
+    // in half 1 that register is column 20, which stays 0, so the partner sum broadcasts it.
+    // Elsewhere each lane half holds half of a row's sum in l_run.
+    constexpr bool LSUM = D == 16;
+    auto row_l = [&](int qb) __attribute__((always_inline)) {
+        if constexpr (LSUM) return partner_sum(o[qb][0][8]);
+        else return partner_sum(l_run[qb]);
     };
 
     // Raise m_used to m_run in the rows where it fell more than kTau behind; l is
@@ -833,7 +846,7 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             bool any = false;
 #pragma unroll
             for (int qb = 0; qb < T::NQB; qb++) {
-                const float lt = partner_sum(l_run[qb]) * __builtin_amdgcn_exp2f(m_used[qb] - m_run[qb]);
+                const float lt = row_l(qb) * __builtin_amdgcn_exp2f(m_used[qb] - m_run[qb]);
                 need_lo[qb] = lt < kLoThresh;
                 any = any || need_lo[qb];
             }
@@ -858,7 +871,11 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         w[1] = __builtin_bit_cast(u32x2, ra)[1];
         w[2] = __builtin_bit_cast(u32x2, rb)[0];
         w[3] = __builtin_bit_cast(u32x2, rb)[1];
-        if (!dv_ok) w = u32x4{0u, 0u, 0u, 0u};
+        if (!dv_ok) {
+            // class 16: ones in column 16 (the row sums), zeros in 17..31
+            const uint32_t f = LSUM && vj == 0 ? E::kOnePairBits : 0u;
+            w = u32x4{f, f, f, f};
+        }
         return __builtin_bit_cast(v8, w);
     };
     // bf16 P carries a 2^-9 relative rounding error; for a row whose normaliser is
@@ -887,10 +904,11 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
                     }
 #pragma unroll
                     for (int dt = 0; dt < ODT; dt++) o[qb][dt] = E::mma(vfrag(vl, t, dt0 + dt), ptl, o[qb][dt]);
+                    if constexpr (!LSUM)
 #pragma unroll
-                    for (int i = 0; i < 4; i++) rs[t >> 1] = sum_pair(rs[t >> 1], s, ptl, qb, t, i);
+                        for (int i = 0; i < 4; i++) rs[t >> 1] = sum_pair(rs[t >> 1], s, ptl, qb, t, i);
                 }
-                sums_into_l(rs, qb);  // (zero for the rows that skip it)
+                if constexpr (!LSUM) sums_into_l(rs, qb);  // (zero for the rows that skip it)
             }
         }
     };
@@ -913,10 +931,11 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
 #pragma unroll
                 for (int qb = 0; qb < T::NQB; qb++) o[qb][dt] = E::mma(a, pt[qb], o[qb][dt]);
             }
+            if constexpr (!LSUM)
 #pragma unroll
-            for (int qb = 0; qb < T::NQB; qb++)
+                for (int qb = 0; qb < T::NQB; qb++)
 #pragma unroll
-                for (int i = 0; i < 4; i++) rs[qb][t >> 1] = sum_pair(rs[qb][t >> 1], s, pt[qb], qb, t, i);
+                    for (int i = 0; i < 4; i++) rs[qb][t >> 1] = sum_pair(rs[qb][t >> 1], s, pt[qb], qb, t, i);
         }
         if constexpr (D != 16) {
             // Order: the reads of two V^T fragments ahead of the MFMA that uses the first
@@ -932,8 +951,9 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             }
             __builtin_amdgcn_sched_group_barrier(0x008, T::NQB * AHEAD, 1);
         }
+        if constexpr (!LSUM)
 #pragma unroll
-        for (int qb = 0; qb < T::NQB; qb++) sums_into_l(rs[qb], qb);
+            for (int qb = 0; qb < T::NQB; qb++) sums_into_l(rs[qb], qb);
         lo_decision();
         if (BF && any_lo) pv_rem(vl, s);
     };
@@ -1271,7 +1291,7 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
     // ---- epilogue: O = O_acc / l, LSE = (m_used + log2 l) ln 2 ----
 #pragma unroll
     for (int qb = 0; qb < T::NQB; qb++) {
-        const float lt = partner_sum(l_run[qb]);
+        const float lt = row_l(qb);
         if (!qvalid[qb]) continue;
         const int i = qi[qb], h = qh[qb];
         const bool nonempty = lt > 0.f;
