@@ -198,6 +198,8 @@ COUNTER_PASSES = (
     "SQ_WAVES GRBM_GUI_ACTIVE",
     "SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAVE_CYCLES "
     "SQ_WAIT_INST_ANY SQ_ACTIVE_INST_LDS SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU2 SQ_WAIT_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_MISC "
+    "SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE",
 )
 
 
@@ -288,6 +290,8 @@ def write_summary(args):
         for d in pmc_dirs:
             c, n = pass_counters(d)
             gui = c["GRBM_GUI_ACTIVE"] / 8.0  # summed over the 8 XCDs, which run in lockstep
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
+                derived["coexec"] = c["SQ_VALU_MFMA_COEXEC_CYCLES"] / (gui * simd)
             if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
                 derived["mfma_busy"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * simd)
                 derived["lds_wait"] = c["SQ_WAIT_INST_LDS"] / c["SQ_WAVE_CYCLES"]
@@ -318,6 +322,11 @@ def write_summary(args):
                          f"(GRBM_GUI_ACTIVE / 8 x {simd} SIMDs) (MFMA issue included)")
             lines.append(f"- shader clock while counting: {derived['clock']:.2f} GHz = GRBM_GUI_ACTIVE / 8 / "
                          f"dispatch duration")
+        if "coexec" in derived and "mfma_busy" in derived:
+            idle = 1.0 - (derived["mfma_busy"] + derived["valu_active"] - derived["coexec"])
+            lines.append(f"- MFMA and VALU both busy: {derived['coexec']:.3f} = SQ_VALU_MFMA_COEXEC_CYCLES / "
+                         f"(GRBM_GUI_ACTIVE / 8 x {simd} SIMDs); neither: {idle:.3f} "
+                         f"(1 - MFMA busy - VALU active + both)")
         if "valu_per_mfma" in derived:
             lines.append(f"- VALU per MFMA: {derived['valu_per_mfma']:.2f} = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / "
                          f"SQ_INSTS_MFMA")
