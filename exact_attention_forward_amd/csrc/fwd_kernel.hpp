@@ -996,7 +996,14 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         // than it saves.)
         if (D != 256 || (wave_live && (!CAUSAL || j0 <= wi_hi + delta))) {
             STile s;
+            // Class 128: the waves raise their priority while issuing the tile's MFMAs, so
+            // a wave with MFMAs ready goes before the other wave's softmax on the SIMD
+            // (two independent work-groups per CU on this loop; varlen causal GQA + bias
+            // -1.7%, its fused-producer form -2.9% time; at class 16 +1.8%, so not there)
+            constexpr bool PRIO = D == 128;
+            if (PRIO) __builtin_amdgcn_s_setprio(1);
             qk(kstage(st), s);
+            if (PRIO) __builtin_amdgcn_s_setprio(0);
             // Three kinds of tile (unmasked, band, other masked), each softmax pass
             // chosen once per tile by a uniform branch. O is only touched in
             // straight-line code (the rescale and PV), so the branches merge no
@@ -1013,7 +1020,9 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             if (fast) exp_fast(s);
             else if (banded) exp_band(s, bb);
             else exp_mask(s, lim);
+            if (PRIO) __builtin_amdgcn_s_setprio(1);
             pv(vstage(st), s);
+            if (PRIO) __builtin_amdgcn_s_setprio(0);
         }
         // tiles issued after kb+1: kb+2 .. min(kb+PREFETCH, kb_end-1)
         wait_tiles_after_next(min(kb + T::PREFETCH, kb_end - 1) - (kb + 1));
