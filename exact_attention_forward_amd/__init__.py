@@ -179,6 +179,38 @@ def _check_tensors(q, k, v, *, varlen, B, Sq, Hq, D, cu_seqlens_q, cu_seqlens_k,
             _require(t.device == dev, f"{name} must be on {dev} like q (it is on {t.device})")
 
 
+def _fwd_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, rel_bias):
+    """Sizes of a forward call from its tensors (dense or varlen), with the layout, contiguity
+    and dtype checks both forward entry points share."""
+    varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
+    if varlen:
+        if q.dim() != 3:
+            raise ValueError("varlen q must be [total_q, Hq, D]")
+        _require(k.dim() == 3 and v.dim() == 3, "varlen k and v must be [total_k, Hkv, D] and [total_k, Hkv, Dv]")
+        Sq, Hq, D = q.shape
+        Sk, Hkv, _ = k.shape
+        B = (cu_seqlens_q if cu_seqlens_q is not None else cu_seqlens_k).numel() - 1
+        if max_seqlen_q is None or max_seqlen_k is None:
+            raise ValueError("varlen needs max_seqlen_q and max_seqlen_k")
+        out_shape, lse_shape = (Sq, Hq, v.shape[-1]), (Hq, Sq)
+    else:
+        if q.dim() != 4:
+            raise ValueError("dense q must be [B, Sq, Hq, D]")
+        _require(k.dim() == 4 and v.dim() == 4, "dense k and v must be [B, Sk, Hkv, D] and [B, Sk, Hkv, Dv]")
+        B, Sq, Hq, D = q.shape
+        _, Sk, Hkv, _ = k.shape
+        max_seqlen_q = max_seqlen_q or 0
+        max_seqlen_k = max_seqlen_k or 0
+        out_shape, lse_shape = (B, Sq, Hq, v.shape[-1]), (B, Hq, Sq)
+    for name, t in (("q", q), ("k", k), ("v", v), ("rel_bias", rel_bias)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.dtype != q.dtype or v.dtype != q.dtype or (rel_bias is not None and rel_bias.dtype != q.dtype):
+        raise AttnError(CODE["ATTN_ERR_BAD_DTYPE"], "q, k, v and rel_bias must share one dtype")
+    return (varlen, B, Sq, Sk, Hq, Hkv, D, v.shape[-1], int(max_seqlen_q), int(max_seqlen_k), out_shape,
+            lse_shape)
+
+
 def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
              cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: Optional[int] = None,
              max_seqlen_k: Optional[int] = None, seqused_k=None, rel_bias=None,
@@ -195,35 +227,8 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
     """
     import torch
     lib = load()
-    varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
-    if varlen:
-        if q.dim() != 3:
-            raise ValueError("varlen q must be [total_q, Hq, D]")
-        _require(k.dim() == 3 and v.dim() == 3, "varlen k and v must be [total_k, Hkv, D] and [total_k, Hkv, Dv]")
-        Sq, Hq, D = q.shape
-        Sk, Hkv, _ = k.shape
-        Dv = v.shape[-1]
-        B = (cu_seqlens_q if cu_seqlens_q is not None else cu_seqlens_k).numel() - 1
-        if max_seqlen_q is None or max_seqlen_k is None:
-            raise ValueError("varlen needs max_seqlen_q and max_seqlen_k")
-        out_shape = (Sq, Hq, Dv)
-        lse_shape = (Hq, Sq)
-    else:
-        if q.dim() != 4:
-            raise ValueError("dense q must be [B, Sq, Hq, D]")
-        _require(k.dim() == 4 and v.dim() == 4, "dense k and v must be [B, Sk, Hkv, D] and [B, Sk, Hkv, Dv]")
-        B, Sq, Hq, D = q.shape
-        _, Sk, Hkv, _ = k.shape
-        Dv = v.shape[-1]
-        max_seqlen_q = max_seqlen_q or 0
-        max_seqlen_k = max_seqlen_k or 0
-        out_shape = (B, Sq, Hq, Dv)
-        lse_shape = (B, Hq, Sq)
-    for name, t in (("q", q), ("k", k), ("v", v), ("rel_bias", rel_bias)):
-        if t is not None and not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if k.dtype != q.dtype or v.dtype != q.dtype or (rel_bias is not None and rel_bias.dtype != q.dtype):
-        raise AttnError(CODE["ATTN_ERR_BAD_DTYPE"], "q, k, v and rel_bias must share one dtype")
+    (varlen, B, Sq, Sk, Hq, Hkv, D, Dv, max_seqlen_q, max_seqlen_k, out_shape,
+     lse_shape) = _fwd_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, rel_bias)
     dtype = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -276,26 +281,8 @@ def attn_fwd_noalloc(q, k, v, *, out, lse=None, causal: bool = False, scale: Opt
     """attn_fwd through attn_fwd_noalloc: no workspace; out (and lse, if wanted) are given by
     the caller, so neither this wrapper nor the library allocates. Returns (out, lse)."""
     lib = load()
-    varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
-    if varlen:
-        _require(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, "varlen q, k, v must be [total, heads, dim]")
-        Sq, Hq, D = q.shape
-        Sk, Hkv, _ = k.shape
-        B = (cu_seqlens_q if cu_seqlens_q is not None else cu_seqlens_k).numel() - 1
-        _require(max_seqlen_q is not None and max_seqlen_k is not None, "varlen needs max_seqlen_q and max_seqlen_k")
-        out_shape, lse_shape = (Sq, Hq, v.shape[-1]), (Hq, Sq)
-    else:
-        _require(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "dense q, k, v must be [B, S, heads, dim]")
-        B, Sq, Hq, D = q.shape
-        _, Sk, Hkv, _ = k.shape
-        max_seqlen_q = max_seqlen_q or 0
-        max_seqlen_k = max_seqlen_k or 0
-        out_shape, lse_shape = (B, Sq, Hq, v.shape[-1]), (B, Hq, Sq)
-    Dv = v.shape[-1]
-    for name, t in (("q", q), ("k", k), ("v", v), ("rel_bias", rel_bias)):
-        _require(t is None or t.is_contiguous(), f"{name} must be contiguous")
-    if k.dtype != q.dtype or v.dtype != q.dtype or (rel_bias is not None and rel_bias.dtype != q.dtype):
-        raise AttnError(CODE["ATTN_ERR_BAD_DTYPE"], "q, k, v and rel_bias must share one dtype")
+    (varlen, B, Sq, Sk, Hq, Hkv, D, Dv, max_seqlen_q, max_seqlen_k, out_shape,
+     lse_shape) = _fwd_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, rel_bias)
     _require(out is not None, "attn_fwd_noalloc needs a caller-given out")
     _check_tensors(q, k, v, varlen=varlen, B=B, Sq=Sq, Hq=Hq, D=D, cu_seqlens_q=cu_seqlens_q,
                    cu_seqlens_k=cu_seqlens_k, seqused_k=seqused_k, rel_bias=rel_bias, rel_r=None,
