@@ -57,8 +57,8 @@ DESCRIPTION = {
     "n1a": "cached prediction fp16 MQA 8:1 D64, q[1,16,8,64] k/v[1,300000,1,64], split-KV",
     "n1b": "cached prediction fp16 MQA 8:1 D64, q[1,64,8,64] k/v[1,300000,1,64], split-KV",
     "n1c": "cached prediction fp16 MQA 8:1 D64, q[1,256,8,64] k/v[1,300000,1,64], split-KV",
-    "n2a": "non-causal MHA bf16 [2,8192,32,48] (head dim 48, on the class-64 kernel)",
-    "n2b": "non-causal MHA bf16 [2,8192,32,72] (head dim 72, on the class-128 kernel)",
+    "n2a": "non-causal MHA bf16 [2,8192,32,48] (head dim 48: class-64 tiles, 48-column arithmetic)",
+    "n2b": "non-causal MHA bf16 [2,8192,32,72] (head dim 72: class-128 tiles, 96-column arithmetic)",
     "n2c": "non-causal MHA bf16 [2,8192,32,128] (head dim 128, for comparison)",
 }
 

@@ -354,8 +354,16 @@ attn_status_t run_fwd(const Plan& pl, const void* q, const void* k, const void* 
     hipError_t e;
     switch (pl.dclass) {
         case 16: e = launch_fwd_d16(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s); break;
-        case 64: e = launch_fwd_d64(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s); break;
-        case 128: e = launch_fwd_d128(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s); break;
+        case 64:
+            // head dims up to 48: the same tiles with the QK contraction narrowed to 48 columns
+            e = (D > Dv ? D : Dv) <= 48 ? launch_fwd_d64_n48(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s)
+                                        : launch_fwd_d64(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s);
+            break;
+        case 128:
+            // head dims up to 96: the same tiles with the arithmetic narrowed to 96 columns
+            e = (D > Dv ? D : Dv) <= 96 ? launch_fwd_d128_n96(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s)
+                                        : launch_fwd_d128(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s);
+            break;
         case 256: e = launch_fwd_d256(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s); break;
         default: return ATTN_ERR_UNSUPPORTED_COMBO;
     }

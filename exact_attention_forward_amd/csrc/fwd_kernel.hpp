@@ -168,11 +168,16 @@ __device__ __forceinline__ void wait_vm_all() { wait_vm_loads<0>(); }
 // same rows; each computes S and the softmax for all of them (identical values)
 // and accumulates a quarter of the V columns, so the PV MFMAs of a tile are shared
 // out instead of all falling to the one wave that holds rows.
-template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT, bool DSPLIT>
+// W (a multiple of 16 up to D) narrows the arithmetic to the first W columns of the class: a
+// call whose head dims fit W runs the class's tile geometry and LDS layout but only the QK
+// steps and O^T blocks that can hold data (head dims 72..96 on class 128, 40..48 on 64).
+template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT, bool DSPLIT, int W>
 __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PER_CU)) attn_fwd_kernel(const FwdParams p) {
     using T = Tile<D, CAUSAL>;
-    static_assert(!DSPLIT || (D == 256 && T::NQB == 1 && T::NW == 4), "dv split: class 256, one row block, four waves");
-    constexpr int ODT = DSPLIT ? T::NDT / 4 : T::NDT;  // dv blocks of O^T this wave accumulates
+    static_assert(!DSPLIT || (D == 256 && T::NQB == 1 && T::NW == 4 && W == D), "dv split: class 256, one row block, four waves");
+    static_assert(W == D || (W < D && W % 16 == 0), "narrowed width: a multiple of 16 below the class");
+    constexpr int NCK = W / 16;  // 16-wide steps of the QK contraction that can hold data
+    constexpr int ODT = DSPLIT ? T::NDT / 4 : (W + 31) / 32;  // dv blocks of O^T this wave accumulates
     using E = Elem<BF>;
     typedef typename E::v8 v8;
     typedef f32x16 STile[T::NQB][T::NKB];
@@ -280,12 +285,12 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
     }
 
     // ---- Q fragments (B operand of S^T = K Q^T): lane holds q[row][16c + 8hf .. +7] ----
-    v8 qf[T::NQB][T::NC];
+    v8 qf[T::NQB][NCK];
 #pragma unroll
     for (int qb = 0; qb < T::NQB; qb++) {
         const uint16_t* qrow = p.q + ((q_off + qi[qb]) * p.Hq + qh[qb]) * (long long)p.D;
 #pragma unroll
-        for (int c = 0; c < T::NC; c++) {
+        for (int c = 0; c < NCK; c++) {
             u32x4 x = {0u, 0u, 0u, 0u};  // columns past D stay zero
             if (qvalid[qb] && 16 * c + 8 * hf < p.D) x = *(const u32x4*)(qrow + 16 * c + 8 * hf);
             qf[qb][c] = __builtin_bit_cast(v8, x);
@@ -392,13 +397,13 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             // all reads of a 32-key block go out before its MFMAs (the compiler
             // barrier keeps them from being sunk back to their uses), so each MFMA
             // finds its operand landed instead of waiting out the LDS latency
-            v8 ka[T::NC];
+            v8 ka[NCK];
 #pragma unroll
-            for (int c = 0; c < T::NC; c++)
+            for (int c = 0; c < NCK; c++)
                 ka[c] = T::LEAN ? *(const v8*)(base + (a0 ^ (32 * c)))
                                 : *(const v8*)(kl + k_granule<D>(kb2 * 32 + l32, 2 * c + hf) * 16);
 #pragma unroll
-            for (int c = 0; c < T::NC; c++)
+            for (int c = 0; c < NCK; c++)
 #pragma unroll
                 for (int qb = 0; qb < T::NQB; qb++) s[qb][kb2] = E::mma(ka[c], qf[qb][c], s[qb][kb2]);
         }
@@ -406,13 +411,13 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         // next block (into the registers it just freed), then the last block's MFMAs
         // (left alone, the compiler read the second block one fragment at a time, each
         // read waited for just before its MFMA; measured c5a -5%, c5b -3% time).
-        __builtin_amdgcn_sched_group_barrier(0x100, T::NC, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NCK, 0);
 #pragma unroll
-        for (int g = 0; g < (T::NKB - 1) * T::NC; g++) {
+        for (int g = 0; g < (T::NKB - 1) * NCK; g++) {
             __builtin_amdgcn_sched_group_barrier(0x008, T::NQB, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, T::NQB * T::NC, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, T::NQB * NCK, 0);
     };
 
     auto partner_max = [](float x) __attribute__((always_inline)) {
@@ -1107,11 +1112,11 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
     auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
     // stage A: S^T of the next tile (K fragments from LDS); exponentials of the current one
     auto stage_a = [&](const char* kl, STile& sn, STile& sc) __attribute__((always_inline)) {
-        constexpr int NM = T::NKB * T::NC;    // fragment steps
-        constexpr int EPM = 16 * T::NKB / NM; // exponentials per step and row block
-        constexpr int AH = T::NC < 4 ? T::NC : 4;  // fragments read ahead
+        constexpr int NM = T::NKB * NCK;      // fragment steps
+        constexpr int NE = 16 * T::NKB;       // exponentials per row block, shared out over the steps
+        constexpr int AH = NCK < 4 ? NCK : 4; // fragments read ahead
         auto kread = [&](int g) __attribute__((always_inline)) {
-            return *(const v8*)(kl + k_granule<D>((g / T::NC) * 32 + l32, 2 * (g % T::NC) + hf) * 16);
+            return *(const v8*)(kl + k_granule<D>((g / NCK) * 32 + l32, 2 * (g % NCK) + hf) * 16);
         };
         v8 ka[NM];
 #pragma unroll
@@ -1119,7 +1124,7 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         fence();
 #pragma unroll
         for (int g = 0; g < NM; g++) {
-            const int kb2 = g / T::NC, c = g % T::NC;
+            const int kb2 = g / NCK, c = g % NCK;
 #pragma unroll
             for (int qb = 0; qb < T::NQB; qb++)
                 sn[qb][kb2] = E::mma(ka[g], qf[qb][c], c == 0 ? f32x16{} : sn[qb][kb2]);
@@ -1127,7 +1132,7 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
 #pragma unroll
             for (int qb = 0; qb < T::NQB; qb++)
 #pragma unroll
-                for (int e = g * EPM; e < (g + 1) * EPM; e++)
+                for (int e = g * NE / NM; e < (g + 1) * NE / NM; e++)
                     sc[qb][e / 16][e % 16] =
                         __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][e / 16][e % 16], p.c2, -m_used[qb]));
             fence();
@@ -1139,8 +1144,7 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         constexpr int NTS = T::BN / 16;         // 16-key steps
         constexpr int NM = NTS * ODT;           // fragment steps
         constexpr int AH = 2;                   // fragments read ahead
-        constexpr int CPM = 8 / ODT;            // conversions of the next step per fragment step
-        constexpr int MPM = 16 * T::NKB / NM;   // maxima per fragment step and row block
+        constexpr int NX = 16 * T::NKB;         // maxima per row block, shared out over the steps
         v8 pt[T::NQB][NTS];
         auto cvt = [&](int qb, int t, int e) __attribute__((always_inline)) {
             pt[qb][t][e] = E::to_elem(sc[qb][t >> 1][8 * (t & 1) + e]);
@@ -1169,14 +1173,14 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             for (int qb = 0; qb < T::NQB; qb++) {
                 if (t + 1 < NTS)
 #pragma unroll
-                    for (int e = dt * CPM; e < (dt + 1) * CPM; e++) cvt(qb, t + 1, e);
+                    for (int e = dt * 8 / ODT; e < (dt + 1) * 8 / ODT; e++) cvt(qb, t + 1, e);
                 // the sums of step t (its 4 pairs over the step's fragments)
 #pragma unroll
                 for (int i = dt * 4 / ODT; i < (dt + 1) * 4 / ODT; i++)
                     rs[qb][t >> 1] = sum_pair(rs[qb][t >> 1], sc, pt[qb][t], qb, t, i);
                 if (with_max)
 #pragma unroll
-                    for (int e = g * MPM; e < (g + 1) * MPM; e++) mx[qb] = fmaxf(mx[qb], sn[qb][e / 16][e % 16]);
+                    for (int e = g * NX / NM; e < (g + 1) * NX / NM; e++) mx[qb] = fmaxf(mx[qb], sn[qb][e / 16][e % 16]);
             }
             fence();
         }
@@ -1342,9 +1346,9 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
 }
 
 // ---- launch helpers ----
-template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT, bool DSPLIT>
+template <int D, int W, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT, bool DSPLIT>
 hipError_t launch_one(const FwdParams& p, hipStream_t s) {
-    const void* fn = (const void*)attn_fwd_kernel<D, BF, CAUSAL, VARLEN, BIAS, SPLIT, DSPLIT>;
+    const void* fn = (const void*)attn_fwd_kernel<D, BF, CAUSAL, VARLEN, BIAS, SPLIT, DSPLIT, W>;
     // bias instances may carry the fused producer's rows past the ring
     using T = Tile<D, CAUSAL>;
     constexpr unsigned lds_max = BIAS ? kLdsBytesPerCU / T::WG_PER_CU : T::LDS;
@@ -1369,23 +1373,24 @@ hipError_t launch_one(const FwdParams& p, hipStream_t s) {
 typedef hipError_t (*FwdLauncher)(const FwdParams&, hipStream_t);
 
 // instance index bits: bf16, causal, varlen, bias, split, dv split
-template <int D, int I>
+template <int D, int W, int I>
 hipError_t launch_idx(const FwdParams& p, hipStream_t s) {
-    return launch_one<D, (I & 1) != 0, (I & 2) != 0, (I & 4) != 0, (I & 8) != 0, (I & 16) != 0,
+    return launch_one<D, W, (I & 1) != 0, (I & 2) != 0, (I & 4) != 0, (I & 8) != 0, (I & 16) != 0,
                       (I & 32) != 0>(p, s);
 }
 
-template <int D, size_t... I>
+template <int D, int W, size_t... I>
 constexpr std::array<FwdLauncher, sizeof...(I)> make_fwd_table(std::index_sequence<I...>) {
-    return {&launch_idx<D, (int)I>...};
+    return {&launch_idx<D, W, (int)I>...};
 }
 
-// dsplit is honoured at class 256 only (the host asks for it only there)
-template <int D>
+// dsplit is honoured at class 256 only (the host asks for it only there); W narrows the
+// arithmetic to the first W columns (see the kernel)
+template <int D, int W = D>
 hipError_t launch_fwd_any(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias, bool split,
                           bool dsplit, hipStream_t s) {
     constexpr bool HAS_DSPLIT = D == 256;
-    static constexpr auto table = make_fwd_table<D>(std::make_index_sequence<HAS_DSPLIT ? 64 : 32>{});
+    static constexpr auto table = make_fwd_table<D, W>(std::make_index_sequence<HAS_DSPLIT ? 64 : 32>{});
     if (dsplit && !HAS_DSPLIT) return hipErrorInvalidValue;
     const int idx = (bf16 ? 1 : 0) | (causal ? 2 : 0) | (varlen ? 4 : 0) | (bias ? 8 : 0) | (split ? 16 : 0) |
                     (dsplit ? 32 : 0);

@@ -88,7 +88,11 @@ hipError_t launch_fwd_d16(const FwdParams& p, bool bf16, bool causal, bool varle
                           bool split, bool dsplit, hipStream_t s);
 hipError_t launch_fwd_d64(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
                           bool split, bool dsplit, hipStream_t s);
+hipError_t launch_fwd_d64_n48(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
+                          bool split, bool dsplit, hipStream_t s);
 hipError_t launch_fwd_d128(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
+                           bool split, bool dsplit, hipStream_t s);
+hipError_t launch_fwd_d128_n96(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
                            bool split, bool dsplit, hipStream_t s);
 hipError_t launch_fwd_d256(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
                            bool split, bool dsplit, hipStream_t s);
