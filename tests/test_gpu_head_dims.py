@@ -64,3 +64,32 @@ def test_decode_rows_share_waves(D, Dv, Sq, G):
                     D=D, Dv=Dv, causal=True, seqused=[2100, 1333, 40], nan_pad=True, num_splits=0,
                     name=f"decode D{D} Dv{Dv} Sq{Sq} G{G}")
     full_check(c)
+
+
+@pytest.mark.parametrize("D,Dv,causal,splits", [(72, 72, False, 1), (96, 80, True, 1), (48, 48, False, 1),
+                                                 (40, 48, True, 3), (88, 64, False, 4)])
+def test_narrowed_equals_zero_padded_full_width(D, Dv, causal, splits):
+    """Head dims that run the narrowed instances (max(D, Dv) <= 96 on class 128, <= 48 on
+    class 64) give bitwise the result of the full-width kernel of their class on the same
+    inputs padded with zero columns: the steps the narrowed kernel leaves out add exact zeros."""
+    import numpy as np
+    dclass = 64 if max(D, Dv) <= 64 else 128
+    g = torch.Generator(device="cpu").manual_seed(7900 + D + Dv)
+    B, Sq, Sk, Hq, Hkv = 2, 150, 333, 4, 2
+    q = torch.randn(B, Sq, Hq, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, Sk, Hkv, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, Sk, Hkv, Dv, generator=g).to(torch.bfloat16)
+
+    def pad(t, width):
+        z = torch.zeros(*t.shape[:-1], width, dtype=t.dtype)
+        z[..., :t.shape[-1]] = t
+        return z
+
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    kw = dict(causal=causal, scale=scale, num_splits=splits)
+    out_n, lse_n = fa.attn_fwd(q.cuda(), k.cuda(), v.cuda(), **kw)
+    out_f, lse_f = fa.attn_fwd(pad(q, dclass).cuda(), pad(k, dclass).cuda(), pad(v, dclass).cuda(), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out_n.view(torch.int16), out_f[..., :Dv].contiguous().view(torch.int16))
+    assert torch.equal(lse_n.view(torch.int32), lse_f.view(torch.int32))
+    assert not out_f[..., Dv:].any()
