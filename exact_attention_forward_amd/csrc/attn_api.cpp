@@ -364,7 +364,12 @@ attn_status_t run_fwd(const Plan& pl, const void* q, const void* k, const void* 
             e = (D > Dv ? D : Dv) <= 96 ? launch_fwd_d128_n96(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s)
                                         : launch_fwd_d128(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s);
             break;
-        case 256: e = launch_fwd_d256(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s); break;
+        case 256:
+            // head dims up to 192 outside the decode form: the arithmetic narrowed to 192 columns
+            e = (D > Dv ? D : Dv) <= 192 && !pl.dsplit
+                    ? launch_fwd_d256_n192(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s)
+                    : launch_fwd_d256(p, bf, causal != 0, pl.varlen, with_bias, split, pl.dsplit, s);
+            break;
         default: return ATTN_ERR_UNSUPPORTED_COMBO;
     }
     if (e != hipSuccess) return ATTN_ERR_HIP;

@@ -170,7 +170,8 @@ __device__ __forceinline__ void wait_vm_all() { wait_vm_loads<0>(); }
 // out instead of all falling to the one wave that holds rows.
 // W (a multiple of 16 up to D) narrows the arithmetic to the first W columns of the class: a
 // call whose head dims fit W runs the class's tile geometry and LDS layout but only the QK
-// steps and O^T blocks that can hold data (head dims 72..96 on class 128, 40..48 on 64).
+// steps and O^T blocks that can hold data (head dims 72..96 on class 128, 40..48 on 64,
+// 136..192 on 256 outside decode).
 template <int D, bool BF, bool CAUSAL, bool VARLEN, bool BIAS, bool SPLIT, bool DSPLIT, int W>
 __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PER_CU)) attn_fwd_kernel(const FwdParams p) {
     using T = Tile<D, CAUSAL>;
@@ -1389,7 +1390,7 @@ constexpr std::array<FwdLauncher, sizeof...(I)> make_fwd_table(std::index_sequen
 template <int D, int W = D>
 hipError_t launch_fwd_any(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias, bool split,
                           bool dsplit, hipStream_t s) {
-    constexpr bool HAS_DSPLIT = D == 256;
+    constexpr bool HAS_DSPLIT = D == 256 && W == D;
     static constexpr auto table = make_fwd_table<D, W>(std::make_index_sequence<HAS_DSPLIT ? 64 : 32>{});
     if (dsplit && !HAS_DSPLIT) return hipErrorInvalidValue;
     const int idx = (bf16 ? 1 : 0) | (causal ? 2 : 0) | (varlen ? 4 : 0) | (bias ? 8 : 0) | (split ? 16 : 0) |

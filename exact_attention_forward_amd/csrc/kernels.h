@@ -96,6 +96,8 @@ hipError_t launch_fwd_d128_n96(const FwdParams& p, bool bf16, bool causal, bool 
                            bool split, bool dsplit, hipStream_t s);
 hipError_t launch_fwd_d256(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
                            bool split, bool dsplit, hipStream_t s);
+hipError_t launch_fwd_d256_n192(const FwdParams& p, bool bf16, bool causal, bool varlen, bool bias,
+                           bool split, bool dsplit, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int Dv, bool bf16, hipStream_t s);
 
 }  // namespace mi355attn

@@ -67,13 +67,15 @@ def test_decode_rows_share_waves(D, Dv, Sq, G):
 
 
 @pytest.mark.parametrize("D,Dv,causal,splits", [(72, 72, False, 1), (96, 80, True, 1), (48, 48, False, 1),
-                                                 (40, 48, True, 3), (88, 64, False, 4)])
+                                                 (40, 48, True, 3), (88, 64, False, 4), (160, 160, False, 1),
+                                                 (136, 192, True, 2), (192, 128, False, 1)])
 def test_narrowed_equals_zero_padded_full_width(D, Dv, causal, splits):
     """Head dims that run the narrowed instances (max(D, Dv) <= 96 on class 128, <= 48 on
-    class 64) give bitwise the result of the full-width kernel of their class on the same
-    inputs padded with zero columns: the steps the narrowed kernel leaves out add exact zeros."""
+    class 64, <= 192 on class 256) give bitwise the result of the full-width kernel of their
+    class on the same inputs padded with zero columns: the steps the narrowed kernel leaves out
+    add exact zeros."""
     import numpy as np
-    dclass = 64 if max(D, Dv) <= 64 else 128
+    dclass = 64 if max(D, Dv) <= 64 else 128 if max(D, Dv) <= 128 else 256
     g = torch.Generator(device="cpu").manual_seed(7900 + D + Dv)
     B, Sq, Sk, Hq, Hkv = 2, 150, 333, 4, 2
     q = torch.randn(B, Sq, Hq, D, generator=g).to(torch.bfloat16)
