@@ -50,11 +50,13 @@ typedef __attribute__((address_space(3))) s16x4v lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLoThresh = 32.f;  // rows with a smaller softmax normaliser get the P remainder MFMA
-constexpr float kTau = 8.f;
+// bfloat16 P: a row whose uncorrected weights may have fewer effective keys than this
+// ((sum p)^2 / sum p^2, from a bound on the squares) gets the P remainder MFMA for the tile
+constexpr float kLoThresh = 64.f;
+constexpr float kTau = 8.f;  // O / l are rescaled only when the row max grows by more than 2^kTau
 // a buffer offset past every range the kernel builds (row bytes x 64 keys stay below it:
 // the host bounds heads x head dim)
-constexpr int kOobOffset = 0x40000000;        // O / l are rescaled only when the row max grows by more than 2^kTau
+constexpr int kOobOffset = 0x40000000;
 
 template <bool BF>
 struct Elem;
@@ -304,11 +306,18 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
     // p = 2^(t - m_used) <= 2^kTau and the rescale is rare after the first tiles.
     f32x16 o[T::NQB][ODT];
     float m_run[T::NQB], m_used[T::NQB], l_run[T::NQB];
+    // bfloat16 P: q_run bounds the sum of squares of the weights O holds without the
+    // remainder correction (scaled with l); l_stop is l when that bookkeeping last paused;
+    // m_tile is the current tile's row max (log2 domain, scaled)
+    float q_run[T::NQB], l_stop[T::NQB], m_tile[T::NQB];
 #pragma unroll
     for (int qb = 0; qb < T::NQB; qb++) {
         m_run[qb] = -INFINITY;
         m_used[qb] = -INFINITY;
         l_run[qb] = 0.f;
+        q_run[qb] = 0.f;
+        l_stop[qb] = 0.f;
+        m_tile[qb] = -INFINITY;
 #pragma unroll
         for (int dt = 0; dt < ODT; dt++)
 #pragma unroll
@@ -456,6 +465,8 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
                 alpha[qb] = __builtin_amdgcn_exp2f(m_used[qb] - m_run[qb]);
                 m_used[qb] = m_run[qb];
                 l_run[qb] *= alpha[qb];
+                q_run[qb] *= alpha[qb] * alpha[qb];
+                l_stop[qb] *= alpha[qb];
                 need = true;
             }
         }
@@ -496,7 +507,8 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             for (int kb2 = 0; kb2 < T::NKB; kb2++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[qb][kb2][r]);
-            m_run[qb] = fmaxf(m_run[qb], partner_max(mx) * p.c2);
+            m_tile[qb] = partner_max(mx) * p.c2;
+            m_run[qb] = fmaxf(m_run[qb], m_tile[qb]);
         }
     };
     auto exp_fast = [&](STile& s) __attribute__((always_inline)) {
@@ -769,7 +781,8 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
                     // a masked key's term is -inf, and so is the FMA (scores are finite)
                     mx = fmaxf(mx, __builtin_fmaf(s[qb][kb2][r], p.c2, band_term(qb, kb2, r, bb)));
                 }
-            m_run[qb] = fmaxf(m_run[qb], partner_max(mx));
+            m_tile[qb] = partner_max(mx);
+            m_run[qb] = fmaxf(m_run[qb], m_tile[qb]);
         }
     };
     auto exp_band = [&](STile& s, const BiasBits& bb) __attribute__((always_inline)) {
@@ -793,7 +806,8 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
 #pragma unroll
                 for (int r = 0; r < 16; r++)
                     mx = fmaxf(mx, lim_vis(lim, qb, kb2, r) ? __builtin_fmaf(s[qb][kb2][r], p.c2, 0.f) : -INFINITY);
-            m_run[qb] = fmaxf(m_run[qb], partner_max(mx));
+            m_tile[qb] = partner_max(mx);
+            m_run[qb] = fmaxf(m_run[qb], m_tile[qb]);
         }
     };
     auto exp_mask = [&](STile& s, const VisLim& lim) __attribute__((always_inline)) {
@@ -847,16 +861,49 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
     // which rows take the remainder MFMA for the tile whose exponentials were just added to l
     bool need_lo[T::NQB];
     bool any_lo = false;
-    auto lo_decision = [&]() __attribute__((always_inline)) {
-        if (BF) {
-            bool any = false;
+    // the remainder test and its bookkeeping run while lo_check holds (wave-uniform)
+    bool lo_check = true;
+    // this lane's share of a row's l (the lane halves hold disjoint keys of the row)
+    auto l_part = [&](int qb) __attribute__((always_inline)) {
+        if constexpr (LSUM) return o[qb][0][8];
+        else return l_run[qb];
+    };
+    // The pause test of one row (l and q: row totals relative to m_used): taken to the row
+    // max, (l + x)^2 >= (q + x) kLoThresh must hold for every x >= 0, i.e. further weights
+    // at or below the max (x: their sum, their squares at most x) cannot bring the row's
+    // effective key count below the threshold. Rows without weight pass.
+    auto pause_ok = [&](int qb, float lt, float qt) __attribute__((always_inline)) {
+        const float f = __builtin_amdgcn_exp2f(m_used[qb] - m_run[qb]);
+        const float l1 = lt * f, q1 = qt * f * f;
+        const float slack = l1 * l1 - q1 * kLoThresh, b = kLoThresh - 2.f * l1;
+        return !(lt > 0.f) || (slack >= 0.f && (b <= 0.f || 4.f * slack >= b * b));
+    };
+    // Some row max grew (m_prev: the maxima before, m_run: after) while the test was
+    // paused. If every row's l, taken to the new max, is still at least kLoThresh, the
+    // pause holds as it is: any q is at most l there (no weight exceeds the max), which
+    // passes pause_ok, and the weights added since the pause stay covered by the bound
+    // below, taken at a later resume with a larger max. Otherwise the weights added since
+    // the pause, each at most 2^(m_prev - m_used), add at most that times their sum to the
+    // squares: q_run takes that bound, and the pause test runs against the new max; the
+    // test resumes if a row fails it or has just seen its first keys. (A rescale scales
+    // l_stop with l.)
+    auto lo_resume = [&](const float (&m_prev)[T::NQB]) __attribute__((always_inline)) {
+        if (BF && !lo_check) {
+            bool low = false;
 #pragma unroll
-            for (int qb = 0; qb < T::NQB; qb++) {
-                const float lt = row_l(qb) * __builtin_amdgcn_exp2f(m_used[qb] - m_run[qb]);
-                need_lo[qb] = lt < kLoThresh;
-                any = any || need_lo[qb];
+            for (int qb = 0; qb < T::NQB; qb++)
+                low = low || row_l(qb) * __builtin_amdgcn_exp2f(m_used[qb] - m_run[qb]) < kLoThresh;
+            if (__any(low)) {
+                bool stay = false;
+#pragma unroll
+                for (int qb = 0; qb < T::NQB; qb++) {
+                    const bool had = m_prev[qb] > -INFINITY;
+                    if (had) q_run[qb] += __builtin_amdgcn_exp2f(m_prev[qb] - m_used[qb]) * (l_part(qb) - l_stop[qb]);
+                    l_stop[qb] = l_part(qb);
+                    stay = stay || (!had && m_run[qb] > -INFINITY) || !pause_ok(qb, row_l(qb), partner_sum(q_run[qb]));
+                }
+                lo_check = __any(stay);
             }
-            any_lo = __any(any);
         }
     };
     // V^T fragment (A operand of O^T += V^T P^T) for keys 16t.. and dv block dt:
@@ -884,12 +931,10 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         }
         return __builtin_bit_cast(v8, w);
     };
-    // bf16 P carries a 2^-9 relative rounding error; for a row whose normaliser is
-    // still small (few keys hold its weight) that error can reach the output
-    // tolerance, so such rows also feed the remainder P - bf16(P) through the MFMA
-    // (after the tile's main product; its rounded weights join l). A row with
-    // normaliser l (max weight 1) has at least l effective keys, and the error
-    // shrinks like 2^-9 / sqrt(3 l); rows at or above kLoThresh skip it.
+    // bf16 P carries a relative rounding error of up to 2^-8 per weight; where few keys
+    // hold a row's weight that error can reach the output tolerance, so such rows also
+    // feed the remainder P - bf16(P) through the MFMA (after the tile's main product; its
+    // rounded weights join l).
     auto pv_rem = [&](const char* vl, const STile& s) __attribute__((always_inline)) {
         if constexpr (BF) {
             // rare: only while some row of the wave has a small normaliser
@@ -918,9 +963,47 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             }
         }
     };
+    // The remainder test, after a tile's weights have joined l (l0: this lane's share of l
+    // before). The rounding errors of the weights O holds uncorrected add up to a relative
+    // error in O with a spread of at most about 2^-8 / sqrt(3 n), n = l^2 / q their
+    // effective key count (q: the sum of their squares; no rescale changes the ratio). q is
+    // kept as a bound: a tile adds at most its row max weight times its row sum. A row
+    // whose bound on n would fall below kLoThresh with this tile takes the remainder for
+    // the tile; the others add the tile's term to q_run. The bookkeeping pauses once every
+    // row passes pause_ok; a new row max tests again (lo_resume).
+    auto lo_step = [&](const char* vl, const STile& s, const float (&l0)[T::NQB]) __attribute__((always_inline)) {
+        if (BF && lo_check) {
+            float lt[T::NQB], qt[T::NQB];
+            bool any = false;
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++) {
+                const float ts = l_part(qb) - l0[qb];  // this lane's share of the tile's row sum
+                const float t2 = ts > 0.f ? __builtin_amdgcn_exp2f(m_tile[qb] - m_used[qb]) * ts : 0.f;
+                const float qn = q_run[qb] + t2;
+                lt[qb] = row_l(qb);
+                qt[qb] = partner_sum(qn);
+                need_lo[qb] = qt[qb] * kLoThresh > lt[qb] * lt[qb];
+                if (!need_lo[qb]) q_run[qb] = qn;
+                any = any || need_lo[qb];
+            }
+            any_lo = __any(any);
+            // (the pause test is evaluated either way: O stays out of the branches)
+            bool stay = any;
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++) stay = stay || !pause_ok(qb, lt[qb], qt[qb]);
+            lo_check = __any(stay);
+            // pausing: no row took the remainder, so l is final for the tile
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++) l_stop[qb] = lo_check ? l_stop[qb] : l_part(qb);
+            if (any_lo) pv_rem(vl, s);
+        }
+    };
     // O^T += V^T P^T, 16 keys per MFMA step, with P formed and summed into l step by
     // step; then the remainder test on the updated l
     auto pv = [&](const char* vl, const STile& s) __attribute__((always_inline)) {
+        float l0[T::NQB];
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) l0[qb] = BF ? l_part(qb) : 0.f;
         float rs[T::NQB][T::NKB];
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++)
@@ -960,8 +1043,7 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         if constexpr (!LSUM)
 #pragma unroll
             for (int qb = 0; qb < T::NQB; qb++) sums_into_l(rs[qb], qb);
-        lo_decision();
-        if (BF && any_lo) pv_rem(vl, s);
+        lo_step(vl, s, l0);
     };
 
     // ---- main loop over key tiles ----
@@ -1018,9 +1100,18 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             const bool banded = BIAS && band;
             VisLim lim;
             if (!fast && !banded) vis_limits(lim, j0);
+            float m_prev[T::NQB];
+#pragma unroll
+            for (int qb = 0; qb < T::NQB; qb++) m_prev[qb] = m_run[qb];
             if (fast) max_fast(s);
             else if (banded) max_band(s, bb);
             else max_mask(s, lim);
+            if (BF && !lo_check) {
+                bool grew = false;
+#pragma unroll
+                for (int qb = 0; qb < T::NQB; qb++) grew = grew || m_run[qb] > m_prev[qb];
+                if (__any(grew)) lo_resume(m_prev);
+            }
             update_used_max();
             rescale_acc();
             if (fast) exp_fast(s);
@@ -1082,28 +1173,22 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         }
     };
     // Commit the maxima; only a row max that grew can call for a rescale (after one,
-    // m_run <= m_used + kTau holds until m_run grows) or make the normaliser relative to
-    // the max fall (lo_check: the remainder test is due).
-    bool lo_check = true;
+    // m_run <= m_used + kTau holds until m_run grows) or resume the remainder test.
     auto commit_max = [&]() __attribute__((always_inline)) {
         bool grew = false;
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) grew = grew || mx_next[qb] > m_run[qb];
         if (__any(grew)) {
             asm volatile("; row max grew" ::: "memory");
+            float m_prev[T::NQB];
 #pragma unroll
-            for (int qb = 0; qb < T::NQB; qb++) m_run[qb] = fmaxf(m_run[qb], mx_next[qb]);
+            for (int qb = 0; qb < T::NQB; qb++) {
+                m_prev[qb] = m_run[qb];
+                m_run[qb] = fmaxf(m_run[qb], mx_next[qb]);
+            }
+            lo_resume(m_prev);
             update_used_max();
             rescale_acc();
-            lo_check = true;
-        }
-    };
-    // after a tile's sums: the remainder test (tile_step's, skipped while it cannot pass)
-    auto lo_step = [&](const char* vl, const STile& s) __attribute__((always_inline)) {
-        if (BF && lo_check) {
-            lo_decision();
-            if (any_lo) pv_rem(vl, s);
-            else lo_check = false;
         }
     };
     // The two stages are written in issue order, one K or V fragment at a time: its
@@ -1154,6 +1239,7 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         float mx[T::NQB];
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
+            m_tile[qb] = mx_next[qb];  // this tile's max (mx_next moves on to the next tile below)
             mx[qb] = -INFINITY;
 #pragma unroll
             for (int kb2 = 0; kb2 < T::NKB; kb2++) rs[qb][kb2] = 0.f;
@@ -1225,9 +1311,12 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         // K of tile r+1+PF goes to K stage st, V of tile r+PF to V stage (st+PF) % NB
         if (r + 1 + PF < ntl) issue_tile(kbase, kb + 1 + PF, kstage(st), false);
         if (r + PF < ntl) issue_tile(vbase, kb + PF, vstage((st + PF) & (T::NB - 1)), true);
+        float l0[T::NQB];
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) l0[qb] = l_part(qb);
         stage_a(kstage((st + 1) & (T::NB - 1)), sn, sc);
         stage_b(vstage(st), sn, sc, true);
-        lo_step(vstage(st), sc);
+        lo_step(vstage(st), sc, l0);
         commit_max();
         // K of tile r+2 and V of tile r+1 must have landed: they were issued before the
         // loads of iterations max(0, r+2-PF) .. r
@@ -1241,10 +1330,13 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
     auto pipe_last = [&](int r, STile& sc, int st) __attribute__((always_inline)) {
         const int kb = kb_begin + r;
         if (r + PF < ntl) issue_tile(vbase, kb + PF, vstage((st + PF) & (T::NB - 1)), true);
+        float l0[T::NQB];
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++) l0[qb] = l_part(qb);
         exp_fast(sc);
         fence();
         stage_b(vstage(st), sc, sc, false);
-        lo_step(vstage(st), sc);
+        lo_step(vstage(st), sc, l0);
         // the tile_step path keeps its own load order: start it with nothing in flight
         wait_vm_all();
         __syncthreads();

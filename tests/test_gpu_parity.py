@@ -240,3 +240,41 @@ def test_short_rows_bf16_accuracy():
     c2 = random_case(901, dtype="bf16", B=0, Sq=0, Sk=0, Hq=4, Hkv=4, D=64, causal=True,
                      varlen_lens=(lens, lens), q_std=4.0, name="short rows bf16 peaked")
     full_check(c2)
+
+
+@pytest.mark.parametrize("D,causal", [(128, False), (128, True), (256, False), (64, False)],
+                         ids=["d128", "d128-causal", "d256", "d64"])
+def test_long_rows_few_effective_keys_bf16(D, causal):
+    """bf16, 2500 keys per row. (1) Peaked scores (q std 3): most weight on a few keys in
+    every tile. (2) A near-tie of three keys late in the row (keys 2100..2102 scaled up),
+    arriving after the remainder bookkeeping has paused, so it must resume: in the rows those
+    keys dominate (>= 90% of the weight), O rounded to bfloat16 must match the correctly
+    rounded oracle in all but a few elements (without the remainder about a quarter differ,
+    by a simulation of the same arithmetic)."""
+    c = random_case(920 + D + causal, dtype="bf16", B=1, Sq=160, Sk=2500, Hq=8, Hkv=2, D=D,
+                    causal=causal, q_std=3.0, name=f"peaked long rows D={D}")
+    full_check(c)
+    c = random_case(930 + D + causal, dtype="bf16", B=1, Sq=160, Sk=2500, Hq=8, Hkv=2, D=D,
+                    causal=causal, name=f"late near-tie D={D}")
+    kf = gen.bits_to_f32(c.k, "bf16").astype(np.float64)
+    kf[:, 2100] *= 8.0
+    kf[:, 2101] = 0.97 * kf[:, 2100]
+    kf[:, 2102] = 0.94 * kf[:, 2100]
+    c.k = gen.to_bits(kf.astype(np.float32), "bf16")
+    out, lse = c.run_gpu()
+    O_ref, L_ref = c.oracle_full()
+    o = host_f64(out, "bf16")
+    check_o(o, O_ref, "bf16", c.name)
+    # weight of the three keys per (row, head), from the inputs and the oracle's LSE
+    qf = gen.bits_to_f32(c.q, "bf16").astype(np.float64)[0]          # [Sq, Hq, D]
+    kt = gen.bits_to_f32(c.k, "bf16").astype(np.float64)[0, 2100:2103]  # [3, Hkv, D]
+    G = c.Hq // c.Hkv
+    s = np.einsum("ihd,jhd->ihj", qf, np.repeat(kt, G, axis=1)) * c.scale
+    w = np.exp(s - L_ref[0].T[:, :, None]).sum(-1)                    # [Sq, Hq]
+    dom = w >= 0.9
+    assert dom.sum() >= 50, f"only {dom.sum()} dominated rows"
+    want = gen.to_bits(O_ref[0].astype(np.float32), "bf16")
+    got = out.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)[0]
+    frac = float((got[dom] != want[dom]).mean())
+    say(f"  {int(dom.sum())} dominated rows: {frac:.4f} of their O elements differ from the rounded oracle")
+    assert frac <= 0.03, f"{c.name}: {frac:.3f} of the dominated rows' elements differ from the rounded oracle"
