@@ -1197,7 +1197,7 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
     // shadow of the MFMAs before it and every fragment is read a few steps ahead of use.
     auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
     // stage A: S^T of the next tile (K fragments from LDS); exponentials of the current one
-    auto stage_a = [&](const char* kl, STile& sn, STile& sc) __attribute__((always_inline)) {
+    auto stage_a = [&](const char* kl, STile& sn, STile& sc, const char* vl, v8 (&vpre)[2]) __attribute__((always_inline)) {
         constexpr int NM = T::NKB * NCK;      // fragment steps
         constexpr int NE = 16 * T::NKB;       // exponentials per row block, shared out over the steps
         constexpr int AH = NCK < 4 ? NCK : 4; // fragments read ahead
@@ -1215,6 +1215,10 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             for (int qb = 0; qb < T::NQB; qb++)
                 sn[qb][kb2] = E::mma(ka[g], qf[qb][c], c == 0 ? f32x16{} : sn[qb][kb2]);
             if (g + AH < NM) ka[g + AH] = kread(g + AH);
+            // stage B's first two V^T fragments go out in the last two steps, which read no K
+            // fragment ahead, so PV finds them landed (c2 -0.3..-1% time, same results)
+            if (g == NM - 2) vpre[0] = vfrag(vl, 0, dt0);
+            if (g == NM - 1) vpre[1] = vfrag(vl, 1 / ODT, dt0 + 1 % ODT);
 #pragma unroll
             for (int qb = 0; qb < T::NQB; qb++)
 #pragma unroll
@@ -1226,7 +1230,7 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
     };
     // stage B: P V of the current tile (V^T fragments from LDS); P in the dtype, its sums
     // into l (tile_step's order) and the row maxima of the next tile
-    auto stage_b = [&](const char* vl, const STile& sn, const STile& sc, bool with_max) __attribute__((always_inline)) {
+    auto stage_b = [&](const char* vl, const STile& sn, const STile& sc, bool with_max, const v8 (&vpre)[2], bool pre) __attribute__((always_inline)) {
         constexpr int NTS = T::BN / 16;         // 16-key steps
         constexpr int NM = NTS * ODT;           // fragment steps
         constexpr int AH = 2;                   // fragments read ahead
@@ -1247,8 +1251,13 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             for (int e = 0; e < 8; e++) cvt(qb, 0, e);
         }
         v8 va[NM];
+        if (pre) {
+            va[0] = vpre[0];
+            va[1] = vpre[1];
+        } else {
 #pragma unroll
-        for (int g = 0; g < AH; g++) va[g] = vfrag(vl, g / ODT, dt0 + g % ODT);
+            for (int g = 0; g < AH; g++) va[g] = vfrag(vl, g / ODT, dt0 + g % ODT);
+        }
         fence();
 #pragma unroll
         for (int g = 0; g < NM; g++) {
@@ -1314,8 +1323,9 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         float l0[T::NQB];
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) l0[qb] = l_part(qb);
-        stage_a(kstage((st + 1) & (T::NB - 1)), sn, sc);
-        stage_b(vstage(st), sn, sc, true);
+        v8 vpre[2];
+        stage_a(kstage((st + 1) & (T::NB - 1)), sn, sc, vstage(st), vpre);
+        stage_b(vstage(st), sn, sc, true, vpre, true);
         lo_step(vstage(st), sc, l0);
         commit_max();
         // K of tile r+2 and V of tile r+1 must have landed: they were issued before the
@@ -1335,7 +1345,8 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         for (int qb = 0; qb < T::NQB; qb++) l0[qb] = l_part(qb);
         exp_fast(sc);
         fence();
-        stage_b(vstage(st), sc, sc, false);
+        v8 vpre[2];
+        stage_b(vstage(st), sc, sc, false, vpre, false);
         lo_step(vstage(st), sc, l0);
         // the tile_step path keeps its own load order: start it with nothing in flight
         wait_vm_all();
