@@ -797,7 +797,23 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
         }
     };
     // (a visible key's term is 0: the same FMA as the fast path, s * c2 - mu)
-    auto max_mask = [&](STile& s, const VisLim& lim) __attribute__((always_inline)) {
+    // Each masked pass takes its own copy of the limits through an empty asm: otherwise the
+    // compiler may form the 32 visibility compares per lane once, ahead of the tile-kind
+    // branch, and keep the masks in scalar register pairs for both passes -- at head-dim
+    // class 16 that spilled 144 scalar registers to vector lanes and ran the compares and
+    // the spills on every tile (c4b +27% time).
+    auto pin_limits = [](VisLim& lm, const VisLim& lim) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < T::NQB; qb++)
+#pragma unroll
+            for (int kb2 = 0; kb2 < T::NKB; kb2++) {
+                lm[qb][kb2] = lim[qb][kb2];
+                asm volatile("" : "+v"(lm[qb][kb2]));
+            }
+    };
+    auto max_mask = [&](STile& s, const VisLim& lim_in) __attribute__((always_inline)) {
+        VisLim lim;
+        pin_limits(lim, lim_in);
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
             float mx = -INFINITY;
@@ -810,7 +826,9 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             m_run[qb] = fmaxf(m_run[qb], m_tile[qb]);
         }
     };
-    auto exp_mask = [&](STile& s, const VisLim& lim) __attribute__((always_inline)) {
+    auto exp_mask = [&](STile& s, const VisLim& lim_in) __attribute__((always_inline)) {
+        VisLim lim;
+        pin_limits(lim, lim_in);
 #pragma unroll
         for (int qb = 0; qb < T::NQB; qb++) {
             const float mu = m_used[qb] == -INFINITY ? 0.f : m_used[qb];
