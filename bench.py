@@ -558,6 +558,75 @@ def decode_summary(r):
             "dtype": r.spec.dtype}
 
 
+def _parse_smi_power(text):
+    """Socket power (W) and per-XCD GFX clocks (MHz) from one `amd-smi metric -p -c` sample."""
+    import re
+    power, clocks, gfx = None, [], False
+    for line in text.splitlines():
+        m = re.match(r"\s*SOCKET_POWER:\s*([0-9.]+)\s*W", line)
+        if m:
+            power = float(m.group(1))
+            continue
+        if re.match(r"\s*GFX_\d+:\s*$", line):
+            gfx = True
+            continue
+        if re.match(r"\s*[A-Z][A-Z0-9_]*:\s*$", line):
+            gfx = False  # another clock domain (memory, video, ...)
+            continue
+        m = re.match(r"\s*CLK:\s*([0-9.]+)\s*MHz", line)
+        if gfx and m:
+            clocks.append(float(m.group(1)))
+    return power, clocks
+
+
+def power_run(fa, q, k, v, kw, seconds, path, workload, dtype):
+    """Keep calling the forward for `seconds` while a child process takes `amd-smi metric -p -c`
+    samples (socket power and GFX clocks); write the samples and their means to `path`."""
+    import subprocess
+    import torch
+    cmd = ["amd-smi", "metric", "-p", "-c", "-g", "0"]
+    torch.cuda.synchronize()
+    time.sleep(3.0)  # the readings are averages over about a second: let the load fade first
+    idle = subprocess.run(cmd, capture_output=True, text=True, timeout=60).stdout
+    samples = []
+    t0 = time.perf_counter()
+    child, t_last = None, t0
+    calls = 0
+    while time.perf_counter() - t0 < seconds:
+        now = time.perf_counter()
+        # one sample a second (the readings refresh about that often), from the second second on
+        if child is None and now - t0 > 1.0 and now - t_last >= 1.0:
+            child, t_last = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                             text=True), now
+        elif child is not None and child.poll() is not None:
+            samples.append(_parse_smi_power(child.stdout.read()))
+            child = None
+        fa.attn_fwd(q, k, v, **kw)
+        calls += 1
+        if calls % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    if child is not None:
+        child.wait()
+    p_idle, c_idle = _parse_smi_power(idle)
+    good = [(p, c) for p, c in samples if p is not None and c]
+    with open(path, "w") as f:
+        f.write(f"# socket power and GFX clocks while {workload} ({DESCRIPTION[workload]}, {dtype}) runs back to back\n")
+        f.write(f"# command: python3 bench.py --no-cpu --decode-steps 0 --workload {workload} --dtype {dtype} "
+                f"--power {os.path.relpath(path, REPO)}\n")
+        f.write("# sampler: amd-smi metric -p -c -g 0 in a child process, one sample a second from the "
+                "second second of load on; idle = 3 s after the timed steps, before this load\n")
+        f.write(f"idle_socket_power_w = {p_idle}\n")
+        for i, (p, c) in enumerate(good):
+            f.write(f"sample_{i} = socket_power_w {p:.0f}, gfx_clock_mhz mean {np.mean(c):.0f} "
+                    f"min {min(c):.0f} max {max(c):.0f} over {len(c)} XCDs\n")
+        if good:
+            f.write(f"mean_socket_power_w = {np.mean([p for p, _ in good]):.0f}\n")
+            f.write(f"mean_gfx_clock_mhz = {np.mean([np.mean(c) for _, c in good]):.0f}\n")
+        f.write(f"calls = {calls}\n")
+    log(open(path).read())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -578,6 +647,10 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the call captured in a HIP graph and replayed (host "
                          "dispatch overhead: eager vs graph microseconds per call)")
+    ap.add_argument("--power", metavar="FILE",
+                    help="after the timed steps, keep calling the forward for --power-seconds while "
+                         "amd-smi samples socket power and GFX clocks; write them to FILE")
+    ap.add_argument("--power-seconds", type=float, default=8.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB elementwise copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -649,6 +722,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
     }
+    if args.power:
+        power_run(fa, q, k, v, kw, args.power_seconds, os.path.abspath(args.power), args.workload, spec.dtype)
     if args.graph:
         result["dispatch"] = graph_timing(fa, q, k, v, kw, args.steps, ms_step, mean_call_ms)
         log(f"dispatch: {result['dispatch']}")
