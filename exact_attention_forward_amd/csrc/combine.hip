@@ -39,13 +39,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // (num_splits <= 256): the max, the sum and the weights exp(LSE_s - LSE) come from one
 // read each, and the weights go to LDS. Then the threads take 16-byte column chunks of
 // the partial rows, SP splits side by side (thread = split slot x chunk), each with
-// UNROLL rows in flight, and the SP partial sums of a chunk meet in LDS in a fixed order.
+// UNROLL rows in flight (the first UNROLL issued before the LSE reduction), and the SP
+// partial sums of a chunk meet in LDS in a fixed order.
 // Splits with weight 0 (empty key ranges) are skipped, whatever their partial holds.
 template <int DV, bool BF>
 __global__ void __launch_bounds__(256) attn_combine_kernel(const CombineParams p) {
     constexpr int CH = DV / 4;     // 16-byte chunks of a row
     constexpr int SP = 256 / CH;   // splits read side by side
-    constexpr int UNROLL = 8;      // partial rows in flight per thread
+    constexpr int UNROLL = 16;     // partial rows in flight per thread
     static_assert(CH * SP == 256, "a row's chunks tile the work-group");
     __shared__ float red[4];
     __shared__ float wts[256];
@@ -67,6 +68,18 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const CombineParams p
     const long long lse_stride = p.rows_q * p.Hq;  // per split
     const float ls = tid < p.ns ? p.lse_part[lidx + (long long)tid * lse_stride] : -INFINITY;
 
+    // The first UNROLL partial rows of this thread's chunk go out before the LSE reduction
+    // (they do not depend on the weights), so their latency and the reduction's overlap.
+    const int c = tid % CH, sg = tid / CH;
+    const bool active = 4 * c < p.Dv;  // Dv <= DV, a multiple of 8: whole chunks
+    const float* op = p.o_part + item * p.Dv + 4 * c;
+    const long long ostride = lse_stride * p.Dv;  // floats between splits
+    f32x4 x0[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; u++)
+        x0[u] = active && sg + SP * u < p.ns ? *(const f32x4*)(op + (long long)(sg + SP * u) * ostride)
+                                            : f32x4{0.f, 0.f, 0.f, 0.f};
+
     // M = max_s LSE_s, LSE = M + ln sum_s exp(LSE_s - M)
     float M = wave_max(ls);
     if (lane == 0) red[wave] = M;
@@ -83,13 +96,15 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const CombineParams p
     wts[tid] = expf(ls - L);  // (unused when L = -inf)
     __syncthreads();
 
-    const int c = tid % CH, sg = tid / CH;
-    const bool active = 4 * c < p.Dv;  // Dv <= DV, a multiple of 8: whole chunks
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (L != -INFINITY && active) {
-        const float* op = p.o_part + item * p.Dv + 4 * c;
-        const long long ostride = lse_stride * p.Dv;  // floats between splits
-        int s = sg;
+#pragma unroll
+        for (int u = 0; u < UNROLL; u++) {
+            const int s0 = sg + SP * u;
+            const float w = s0 < p.ns ? wts[s0] : 0.f;
+            if (w != 0.f) acc += w * x0[u];
+        }
+        int s = sg + SP * UNROLL;
         for (; s + SP * (UNROLL - 1) < p.ns; s += SP * UNROLL) {
             f32x4 x[UNROLL];
 #pragma unroll
