@@ -32,13 +32,33 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
+# per-kernel register, spill, occupancy and LDS figures the compiler reports, kept beside
+# the objects (tests/test_kernel_resources.py reads them)
+RESOURCES = os.path.join(BUILD, "kernel_resources.txt")
+
+
+def _resources(stderr: str) -> list[str]:
+    """'<kernel> <key>: <value>' lines from the compiler's kernel-resource-usage remarks."""
+    out, name = [], None
+    for line in stderr.splitlines():
+        if "[-Rpass-analysis=kernel-resource-usage]" not in line or "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].replace("[-Rpass-analysis=kernel-resource-usage]", "").strip()
+        if body.startswith("Function Name:"):
+            name = body.split(":", 1)[1].strip()
+        elif name and ":" in body:
+            out.append(f"{name} {body}")
+    return out
+
+
+def _compile(src: str) -> tuple[str, list[str]]:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
+    cmd = [HIPCC] + COMMON + extra + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    return obj
+    return obj, _resources(r.stderr)
 
 
 def build(jobs: int = 8, verbose: bool = False) -> str:
@@ -46,7 +66,12 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, srcs))
+        done = list(ex.map(_compile, srcs))
+    objs = [o for o, _ in done]
+    with open(RESOURCES, "w") as f:
+        for _, lines in done:
+            for line in lines:
+                f.write(line + "\n")
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
