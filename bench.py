@@ -582,8 +582,11 @@ def _parse_smi_power(text):
 def power_run(fa, q, k, v, kw, seconds, path, workload, dtype):
     """Keep calling the forward for `seconds` while a child process takes `amd-smi metric -p -c`
     samples (socket power and GFX clocks); write the samples and their means to `path`."""
+    import shutil
     import subprocess
     import torch
+    if shutil.which("amd-smi") is None:
+        raise SystemExit("bench.py --power needs amd-smi on PATH")
     cmd = ["amd-smi", "metric", "-p", "-c", "-g", "0"]
     torch.cuda.synchronize()
     time.sleep(3.0)  # the readings are averages over about a second: let the load fade first
