@@ -81,7 +81,8 @@ typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1 } attn_dtype_t;
  *   varlen (both cu_seqlens given, int32 [B+1], non-decreasing, first 0, last = total):
  *     Sq = total_q, Sk = total_k;  q [total_q, Hq, D], k [total_k, Hkv, D],
  *     v [total_k, Hkv, Dv], out [total_q, Hq, Dv], lse [Hq, total_q] (fp32)
- *     max_seqlen_q / max_seqlen_k >= every per-sequence length (used to size the grid).
+ *     max_seqlen_q / max_seqlen_k >= every per-sequence length and <= total_q / total_k
+ *     (used to size the grid; 0 only when that total is 0), else ATTN_ERR_BAD_VARLEN.
  *   Sequence b has q_len = Sq (dense) or cu_seqlens_q[b+1] - cu_seqlens_q[b],
  *   and k_len = seqused_k[b] if seqused_k != NULL (device int32 [B], keys
  *   past it are never read into the result, whatever they hold), else Sk or

@@ -170,7 +170,9 @@ def random_case(rng_seed, *, dtype, B, Sq, Sk, Hq, Hkv, D, Dv=None, causal=False
         qls, kls = varlen_lens
         cu_q, cu_k = gen.cu_seqlens(qls), gen.cu_seqlens(kls)
         Sq, Sk, B = int(cu_q[-1]), int(cu_k[-1]), len(qls)
-        max_q, max_k = max(1, max(qls)), max(1, max(kls))
+        # the longest sequence of each side (0 when every sequence of that side is empty: the
+        # library takes max_seqlen <= the total length)
+        max_q, max_k = max(qls), max(kls)
         qshape, kshape, vshape = (Sq, Hq, D), (Sk, Hkv, D), (Sk, Hkv, Dv)
         rows_q = Sq
     else:

@@ -95,6 +95,19 @@ def test_standalone_combine(cfg):
         assert np.isneginf(L_ref).any(), "the case should hold rows with no visible key"
 
 
+# A varlen batch whose query side, or key side, is empty in every sequence: max_seqlen is then
+# 0 on that side. No query rows: nothing is launched or written. No keys: every row is empty
+# (O = 0, LSE = -inf).
+@pytest.mark.parametrize("qls,kls,splits", [([0], [112], 1), ([0, 0, 0], [5, 0, 300], 0),
+                                             ([40, 0, 7], [0, 0, 0], 1), ([40, 0, 7], [0, 0, 0], 3)])
+def test_varlen_side_entirely_empty(qls, kls, splits):
+    c = random_case(930 + len(qls), dtype="fp16", B=len(qls), Sq=0, Sk=0, Hq=8, Hkv=2, D=136, Dv=32,
+                    causal=True, varlen_lens=(qls, kls), num_splits=splits,
+                    name=f"varlen q {qls} k {kls} ns{splits}")
+    say(f"  GPU {c.name}")
+    full_check(c)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.125, -1.5])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_nonpositive_scale(scale, dtype):
