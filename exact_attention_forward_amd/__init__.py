@@ -112,6 +112,10 @@ def _check(status: int):
 def _stream_handle(stream, device):
     import torch
     if stream is None:
+        # torch's current stream on the device, as a raw handle (without building a Stream object)
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return raw(device.index if device.index is not None else torch.cuda.current_device())
         stream = torch.cuda.current_stream(device)
     return stream.cuda_stream
 
@@ -136,47 +140,55 @@ def _check_tensors(q, k, v, *, varlen, B, Sq, Hq, D, cu_seqlens_q, cu_seqlens_k,
                    rel_r, rel_proj, out, lse, workspace, out_shape, lse_shape):
     """Shape, dtype, layout and device checks done before any pointer reaches the library
     (the C entry points see only pointers and sizes, so a wrong tensor would be read or
-    written out of bounds)."""
+    written out of bounds). Messages are formed only for a failing check: this runs on
+    every call, and short calls are dominated by host time."""
     import torch
     nd = 3 if varlen else 4
-    _require(k.dim() == nd and v.dim() == nd, f"k and v must have q's rank ({nd})")
+    if k.dim() != nd or v.dim() != nd:
+        raise ValueError(f"k and v must have q's rank ({nd})")
+    ks, vs = k.shape, v.shape
     if varlen:
-        _require(k.shape[2] == D, f"k {tuple(k.shape)} must be [total_k, Hkv, D={D}]")
-        _require(v.shape[:2] == k.shape[:2], f"v {tuple(v.shape)} must be [total_k, Hkv, Dv] like k")
+        if ks[2] != D:
+            raise ValueError(f"k {tuple(ks)} must be [total_k, Hkv, D={D}]")
+        if vs[:2] != ks[:2]:
+            raise ValueError(f"v {tuple(vs)} must be [total_k, Hkv, Dv] like k")
     else:
-        _require(k.shape[0] == B and k.shape[3] == D, f"k {tuple(k.shape)} must be [B={B}, Sk, Hkv, D={D}]")
-        _require(v.shape[:3] == k.shape[:3], f"v {tuple(v.shape)} must be [B, Sk, Hkv, Dv] like k")
+        if ks[0] != B or ks[3] != D:
+            raise ValueError(f"k {tuple(ks)} must be [B={B}, Sk, Hkv, D={D}]")
+        if vs[:3] != ks[:3]:
+            raise ValueError(f"v {tuple(vs)} must be [B, Sk, Hkv, Dv] like k")
+    i32 = torch.int32
     for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
-        if t is not None:
-            _require(t.dtype == torch.int32 and t.dim() == 1 and t.numel() == B + 1 and t.is_contiguous(),
-                     f"{name} must be a contiguous int32 tensor of B + 1 = {B + 1} elements")
-    if seqused_k is not None:
-        _require(seqused_k.dtype == torch.int32 and seqused_k.dim() == 1 and seqused_k.numel() == B and
-                 seqused_k.is_contiguous(), f"seqused_k must be a contiguous int32 tensor of B = {B} elements")
+        if t is not None and not (t.dtype == i32 and t.dim() == 1 and t.numel() == B + 1 and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 tensor of B + 1 = {B + 1} elements")
+    if seqused_k is not None and not (seqused_k.dtype == i32 and seqused_k.dim() == 1 and
+                                      seqused_k.numel() == B and seqused_k.is_contiguous()):
+        raise ValueError(f"seqused_k must be a contiguous int32 tensor of B = {B} elements")
     rows_q = Sq if varlen else B * Sq
     if rel_bias is not None:
-        _require(rel_bias.dim() == 3 and rel_bias.shape[0] == rows_q and rel_bias.shape[1] == Hq,
-                 f"rel_bias {tuple(rel_bias.shape)} must be [rows_q={rows_q}, Hq={Hq}, rel_extent]")
+        if not (rel_bias.dim() == 3 and rel_bias.shape[0] == rows_q and rel_bias.shape[1] == Hq):
+            raise ValueError(f"rel_bias {tuple(rel_bias.shape)} must be [rows_q={rows_q}, Hq={Hq}, rel_extent]")
     if rel_r is not None:
-        _require(rel_r.dim() == 3 and rel_r.shape[0] == rows_q and rel_r.shape[1] == Hq,
-                 f"rel_r {tuple(rel_r.shape)} must be [rows_q={rows_q}, Hq={Hq}, d_rel]")
-        _require(rel_proj.dim() == 2 and rel_proj.shape[0] == rel_r.shape[2],
-                 f"rel_proj {tuple(rel_proj.shape)} must be [d_rel={rel_r.shape[2]}, rel_extent]")
-    if out is not None:
-        _require(tuple(out.shape) == tuple(out_shape) and out.dtype == q.dtype and out.is_contiguous(),
-                 f"out must be a contiguous {q.dtype} tensor of shape {tuple(out_shape)}")
-    if lse is not None:
-        _require(tuple(lse.shape) == tuple(lse_shape) and lse.dtype == torch.float32 and lse.is_contiguous(),
-                 f"lse must be a contiguous float32 tensor of shape {tuple(lse_shape)}")
-    if workspace is not None:
-        _require(workspace.is_contiguous(), "workspace must be contiguous")
-    dev = q.device
-    _require(dev.type == "cuda", "q must be a CUDA (ROCm) tensor: the forward runs only on the GPU")
-    for name, t in (("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
-                    ("seqused_k", seqused_k), ("rel_bias", rel_bias), ("rel_r", rel_r), ("rel_proj", rel_proj),
-                    ("out", out), ("lse", lse), ("workspace", workspace)):
-        if t is not None:
-            _require(t.device == dev, f"{name} must be on {dev} like q (it is on {t.device})")
+        if not (rel_r.dim() == 3 and rel_r.shape[0] == rows_q and rel_r.shape[1] == Hq):
+            raise ValueError(f"rel_r {tuple(rel_r.shape)} must be [rows_q={rows_q}, Hq={Hq}, d_rel]")
+        if not (rel_proj.dim() == 2 and rel_proj.shape[0] == rel_r.shape[2]):
+            raise ValueError(f"rel_proj {tuple(rel_proj.shape)} must be [d_rel={rel_r.shape[2]}, rel_extent]")
+    if out is not None and not (out.shape == out_shape and out.dtype == q.dtype and out.is_contiguous()):
+        raise ValueError(f"out must be a contiguous {q.dtype} tensor of shape {tuple(out_shape)}")
+    if lse is not None and not (lse.shape == lse_shape and lse.dtype == torch.float32 and lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {tuple(lse_shape)}")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if not q.is_cuda:
+        raise ValueError("q must be a CUDA (ROCm) tensor: the forward runs only on the GPU")
+    dev = q.get_device()
+    for t in (k, v, cu_seqlens_q, cu_seqlens_k, seqused_k, rel_bias, rel_r, rel_proj, out, lse, workspace):
+        if t is not None and t.get_device() != dev:
+            for name, u in (("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
+                            ("seqused_k", seqused_k), ("rel_bias", rel_bias), ("rel_r", rel_r),
+                            ("rel_proj", rel_proj), ("out", out), ("lse", lse), ("workspace", workspace)):
+                if u is t:
+                    raise ValueError(f"{name} must be on {q.device} like q (it is on {t.device})")
 
 
 def _fwd_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, rel_bias):
@@ -249,15 +261,16 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
     E = 0 if rel_bias is None else int(rel_bias.shape[-1])
     if rel_proj is not None:
         E = int(rel_proj.shape[1])
-    ns = lib.attn_num_splits(B, Sq, Sk, Hq, Hkv, D, Dv, int(bool(causal)), int(varlen), max_seqlen_q,
-                             max_seqlen_k, pack_gqa, num_splits)
-    ws_bytes = 0
-    if ns > 1:
-        ws_bytes = lib.attn_fwd_workspace_size(B, Sq, Hq, Dv, int(varlen), ns)
-        if workspace is None:
+    if workspace is not None:
+        # the library checks that the given workspace holds the split partials it needs
+        ws_bytes = workspace.numel() * workspace.element_size()
+    else:
+        ns = lib.attn_num_splits(B, Sq, Sk, Hq, Hkv, D, Dv, int(bool(causal)), int(varlen), max_seqlen_q,
+                                 max_seqlen_k, pack_gqa, num_splits)
+        ws_bytes = 0
+        if ns > 1:
+            ws_bytes = lib.attn_fwd_workspace_size(B, Sq, Hq, Dv, int(varlen), ns)
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-        else:
-            ws_bytes = workspace.numel() * workspace.element_size()
     if rel_r is not None:
         st = lib.attn_fwd_rel_proj(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D,
                                    Dv, float(scale), int(bool(causal)), _ptr(cu_seqlens_q),
