@@ -1269,6 +1269,7 @@ __global__ void __launch_bounds__((Tile<D, CAUSAL>::NT), (Tile<D, CAUSAL>::WG_PE
             for (int e = 0; e < 8; e++) cvt(qb, 0, e);
         }
         v8 va[NM];
+        static_assert(AH == 2, "stage A reads the first two fragments ahead (vpre)");
         if (pre) {
             va[0] = vpre[0];
             va[1] = vpre[1];
