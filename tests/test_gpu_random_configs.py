@@ -66,3 +66,17 @@ def test_random_config(case_no):
     say(f"  case {case_no}: {kw if 'varlen_lens' not in kw else {**kw, 'varlen_lens': '...'}}")
     c = random_case(91_000 + case_no, name=f"random case {case_no}", **kw)
     full_check(c)
+
+
+N_PEAKED = 100
+
+
+@pytest.mark.parametrize("case_no", range(N_PEAKED))
+def test_random_config_peaked_bf16(case_no):
+    """The same draws in bf16 with peaked rows (q std 2, 3, 4): few keys hold a row's weight,
+    where the rounding of P to bf16 matters most and the remainder correction must engage."""
+    kw = dict(draw(case_no), dtype="bf16")
+    q_std = (2.0, 3.0, 4.0)[case_no % 3]
+    say(f"  peaked case {case_no} (q std {q_std})")
+    c = random_case(95_000 + case_no, name=f"peaked case {case_no}", q_std=q_std, **kw)
+    full_check(c)
