@@ -11,12 +11,15 @@
   sentinel; nothing outside them may change (dense, varlen + bias, split, decode, Dv
   below its class).
 """
+import math
+
 import numpy as np
 import pytest
 import torch
 
 import exact_attention_forward_amd as fa
-from tests.gpu_common import check_lse, check_o, dev16, dev_i32, full_check, host_f64, random_case, say
+from tests.gpu_common import LSE_TOL, Case, check_lse, check_o, dev16, dev_i32, full_check, host_f64, random_case, say
+from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
@@ -106,6 +109,47 @@ def test_varlen_side_entirely_empty(qls, kls, splits):
                     name=f"varlen q {qls} k {kls} ns{splits}")
     say(f"  GPU {c.name}")
     full_check(c)
+
+
+# The largest K / V tile the validation accepts: a 64-key tile of Hkv heads spans 2^30 bytes at
+# head dim 128 (Hkv = 2^16) and just under it at 120 (Hkv = 69905, narrowed columns past D), so the
+# buffer ranges, the per-lane load offsets and the past-the-range offset of the padding columns
+# run at their limit. Q, K and V are zero but for a few heads drawn from the generator: those are
+# checked against the oracle, and every other head must give O = 0 and LSE = ln(Sk) (equal
+# scores over zero values).
+@pytest.mark.parametrize("D", [128, 120])
+def test_largest_kv_tile(D):
+    dtype, B, Sq, Sk = "bf16", 1, 2, 200
+    Hkv = (1 << 30) // (64 * D * 2)
+    heads = [0, 1, Hkv // 2, Hkv - 2, Hkv - 1]
+    say(f"  GPU largest K/V tile: D={D} Hkv={Hkv} Sk={Sk}, {64 * Hkv * D * 2} bytes per 64-key tile")
+    tdt = torch.bfloat16
+    q = torch.zeros((B, Sq, Hkv, D), dtype=tdt, device="cuda")
+    k = torch.zeros((B, Sk, Hkv, D), dtype=tdt, device="cuda")
+    v = torch.zeros((B, Sk, Hkv, D), dtype=tdt, device="cuda")
+    cases = []
+    for j, h in enumerate(heads):
+        qh = gen.stream_normal_bits(970 + j, 1, (B, Sq, 1, D), dtype)
+        kh = gen.stream_normal_bits(970 + j, 2, (B, Sk, 1, D), dtype)
+        vh = gen.stream_normal_bits(970 + j, 3, (B, Sk, 1, D), dtype)
+        q[:, :, h:h + 1] = dev16(qh, dtype)
+        k[:, :, h:h + 1] = dev16(kh, dtype)
+        v[:, :, h:h + 1] = dev16(vh, dtype)
+        cases.append(Case(dtype=dtype, B=B, Sq=Sq, Sk=Sk, Hq=1, Hkv=1, D=D, q=qh, k=kh, v=vh,
+                          name=f"largest tile D{D} head {h}"))
+    out, lse = fa.attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    for h, c in zip(heads, cases):
+        O_ref, L_ref = c.oracle_full()
+        check_o(host_f64(out[:, :, h:h + 1], dtype), O_ref, dtype, c.name)
+        check_lse(lse[:, h:h + 1].cpu().numpy().astype(np.float64), L_ref, c.name)
+    rest = torch.ones(Hkv, dtype=torch.bool, device="cuda")
+    rest[heads] = False
+    assert int(torch.count_nonzero(out[:, :, rest])) == 0, "heads with zero inputs must give O = 0"
+    err = float((lse[:, rest].double() - math.log(Sk)).abs().max())
+    assert err <= LSE_TOL, f"heads with zero inputs: LSE off ln(Sk) by {err:.3e}"
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.125, -1.5])
