@@ -152,6 +152,37 @@ def test_largest_kv_tile(D):
     torch.cuda.empty_cache()
 
 
+# Outputs of more than 2^31 elements (rows_q * Hq * Dv): the Q loads and O stores index past any
+# 32-bit range. Q is zero but for rows at both ends drawn from the generator; the call is
+# non-causal, so each checked row is the oracle's row of a small case with the same K and V.
+def test_outputs_beyond_2_31_elements():
+    dtype, B, Sq, Sk, H, D = "bf16", 1, 163840, 96, 128, 128
+    assert B * Sq * H * D > 1 << 31
+    rows = [0, 1, Sq // 2, Sq - 2, Sq - 1]
+    say(f"  GPU outputs beyond 2^31 elements: [{B},{Sq},{H},{D}] ({B * Sq * H * D} elements)")
+    kh = gen.stream_normal_bits(980, 2, (B, Sk, H, D), dtype)
+    vh = gen.stream_normal_bits(980, 3, (B, Sk, H, D), dtype)
+    qh = gen.stream_normal_bits(980, 1, (B, len(rows), H, D), dtype)
+    q = torch.zeros((B, Sq, H, D), dtype=torch.bfloat16, device="cuda")
+    for j, i in enumerate(rows):
+        q[:, i:i + 1] = dev16(qh[:, j:j + 1], dtype)
+    out, lse = fa.attn_fwd(q, dev16(kh, dtype), dev16(vh, dtype))
+    torch.cuda.synchronize()
+    c = Case(dtype=dtype, B=B, Sq=len(rows), Sk=Sk, Hq=H, Hkv=H, D=D, q=qh, k=kh, v=vh,
+             name="rows of a [1,163840,128,128] call")
+    O_ref, L_ref = c.oracle_full()
+    check_o(host_f64(out[:, rows], dtype), O_ref, dtype, c.name)
+    check_lse(lse[:, :, rows].cpu().numpy().astype(np.float64), L_ref, c.name)
+    # a zero query row weighs every key equally: O is the mean of V, LSE = ln(Sk)
+    zero = host_f64(out[:, Sq - 3:Sq - 2], dtype)[0, 0]
+    mean_v = gen.bits_to_f32(vh, dtype).astype(np.float64)[0].mean(axis=0)
+    check_o(zero[None, None], mean_v[None, None], dtype, "zero query row near the end")
+    err = float((lse[:, :, Sq - 3].double() - math.log(Sk)).abs().max())
+    assert err <= LSE_TOL, f"zero query row: LSE off ln(Sk) by {err:.3e}"
+    del q, out, lse
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.125, -1.5])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_nonpositive_scale(scale, dtype):
