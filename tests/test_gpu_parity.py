@@ -141,6 +141,20 @@ def test_grid_beyond_65535_batches():
     check_lse(lv[rows[:, 0], 0, rows[:, 2]], l_ref, "grid")
 
 
+def test_varlen_beyond_65535_sequences():
+    # 70000 varlen sequences of 0..3 query and key rows (empty ones among them), causal,
+    # pack-GQA 2:1 with a bias band: the per-sequence offsets, the chunk-wise XCD deal and the
+    # 1-D grid at a sequence count far above 65535, against the full oracle
+    rng = gen.make_rng(810)
+    B = 70000
+    qls = [int(x) for x in rng.integers(0, 4, B)]
+    kls = [int(x) for x in rng.integers(0, 4, B)]
+    c = random_case(811, dtype="fp16", B=B, Sq=0, Sk=0, Hq=2, Hkv=1, D=64, causal=True,
+                    varlen_lens=(qls, kls), E=128, name="70000 varlen sequences")
+    say(f"  GPU {c.name}: total_q {sum(qls)}, total_k {sum(kls)}")
+    full_check(c)
+
+
 # ---------------------------------------------------------------- bit-exact probes
 
 def _probe_visibility(dtype, B, Sq, Sk, Hq, Hkv, causal, cu=None, seqused=None, pack=-1, ns=1):
