@@ -134,14 +134,101 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const CombineParams p
     if (p.lse && tid == 0) p.lse[lidx] = L;
 }
 
+// One wave per (query row, head), four per work-group, for calls with many rows and at
+// most 64 splits: lane s holds split s's LSE, so the max, the sum and the weights stay in
+// registers (no LDS, no barrier), and the wave's lanes take 16-byte column chunks, SPW
+// splits side by side, U partial rows in flight per lane. The per-work-group fixed cost
+// of the kernel above (three barriers and an LDS round trip per row) is what bounds it
+// when a row has only a few partials to read.
+template <int DV, bool BF>
+__global__ void __launch_bounds__(256) attn_combine_rows_kernel(const CombineParams p) {
+    constexpr int CH = DV / 4;   // 16-byte chunks of a row
+    constexpr int SPW = 64 / CH; // splits read side by side
+    constexpr int U = 8;         // partial rows in flight per lane
+    static_assert(CH * SPW == 64, "a row's chunks tile the wave");
+    const int lane = threadIdx.x & 63;
+    const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= p.rows_q * p.Hq) return;  // uniform over the wave
+    const long long t = item / p.Hq;
+    const int h = (int)(item % p.Hq);
+    long long lidx;
+    if (p.is_varlen) {
+        lidx = (long long)h * p.rows_q + t;
+    } else {
+        const long long bb = t / p.Sq;
+        const long long i = t % p.Sq;
+        lidx = (bb * p.Hq + h) * p.Sq + i;
+    }
+    const long long lse_stride = p.rows_q * p.Hq;  // per split
+    const float ls = lane < p.ns ? p.lse_part[lidx + (long long)lane * lse_stride] : -INFINITY;
+
+    // M = max_s LSE_s, LSE = M + ln sum_s exp(LSE_s - M); both uniform over the wave
+    const float M = wave_max(ls);
+    float L = -INFINITY;
+    if (M != -INFINITY) L = M + logf(wave_sum(expf(ls - M)));
+    const float wl = expf(ls - L);  // split `lane`'s weight (unused when L = -inf)
+
+    const int c = lane % CH, sg = lane / CH;
+    const bool active = 4 * c < p.Dv;  // Dv <= DV, a multiple of 8: whole chunks
+    const float* op = p.o_part + item * p.Dv + 4 * c;
+    const long long ostride = lse_stride * p.Dv;  // floats between splits
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (L != -INFINITY) {  // every lane of the wave takes part in the shuffles below
+        for (int s0 = 0; s0 < p.ns; s0 += SPW * U) {
+            f32x4 x[U];
+            float w[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int sp = s0 + sg + SPW * u;
+                const float wu = __shfl(wl, sp < 64 ? sp : 0, 64);
+                w[u] = sp < p.ns ? wu : 0.f;
+                // splits with weight 0 (empty key ranges) are neither read nor added
+                x[u] = active && w[u] != 0.f ? *(const f32x4*)(op + (long long)sp * ostride)
+                                             : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                if (w[u] != 0.f) acc += w[u] * x[u];
+        }
+    }
+    // the SPW partial sums of a chunk, added in slot order
+    f32x4 o = acc;
+#pragma unroll
+    for (int g = 1; g < SPW; g++) {
+        const int src = c + g * CH;
+        o[0] += __shfl(acc[0], src, 64);
+        o[1] += __shfl(acc[1], src, 64);
+        o[2] += __shfl(acc[2], src, 64);
+        o[3] += __shfl(acc[3], src, 64);
+    }
+    if (sg == 0 && active) {
+        uint16_t* dst = p.out + item * p.Dv + 4 * c;
+        const unsigned lo = (unsigned)narrow<BF>(o[0]) | ((unsigned)narrow<BF>(o[1]) << 16);
+        const unsigned hi = (unsigned)narrow<BF>(o[2]) | ((unsigned)narrow<BF>(o[3]) << 16);
+        *(uint2*)dst = make_uint2(lo, hi);
+    }
+    if (p.lse && lane == 0) p.lse[lidx] = L;
+}
+
+// Calls with at least this many (row, head) items and at most 64 splits take the
+// wave-per-row kernel: enough waves to fill the chip several times over, so the merge is
+// bound by its reads, not by a work-group's fixed cost.
+constexpr long long kRowsCombineMinItems = 8192;
+
 template <int DV, bool BF>
 hipError_t launch_combine_t(const CombineParams& p, hipStream_t s) {
-    const long long blocks = p.rows_q * p.Hq;  // one work-group per (query row, head)
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    const long long items = p.rows_q * p.Hq;
+    if (items <= 0) return hipSuccess;
     CombineParams pp = p;
     void* args[] = {(void*)&pp};
-    return hipLaunchKernel((const void*)attn_combine_kernel<DV, BF>, dim3((unsigned)blocks), dim3(256), args,
+    if (p.ns <= 64 && items >= kRowsCombineMinItems) {
+        const long long blocks = (items + 3) / 4;  // four waves, four items per work-group
+        if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+        return hipLaunchKernel((const void*)attn_combine_rows_kernel<DV, BF>, dim3((unsigned)blocks), dim3(256),
+                               args, 0, s);
+    }
+    if (items > 0x7fffffffLL) return hipErrorInvalidValue;  // one work-group per (query row, head)
+    return hipLaunchKernel((const void*)attn_combine_kernel<DV, BF>, dim3((unsigned)items), dim3(256), args,
                            0, s);
 }
 

@@ -3,8 +3,9 @@
 - attn_combine called on its own (the split-KV merge outside the forward call that the
   returned LSE allows: TabPFN issue #1235, closing comment) on the partials attn_fwd left
   in a caller-owned workspace: dense and varlen LSE layouts, Dv below its head-dim class,
-  rows whose splits are all empty; bitwise equal to attn_fwd's own merge and within the
-  tolerance of the oracle.
+  rows whose splits are all empty, few rows with many splits (a work-group per row) and many
+  rows with few splits (a wave per row); bitwise equal to attn_fwd's own merge and within
+  the tolerance of the oracle.
 - scale = 0 and a negative scale (every tile then takes the masked softmax pass).
 - lse = NULL, with and without splits.
 - guard bands: out, lse and the workspace sit inside larger buffers filled with a
@@ -64,6 +65,16 @@ COMBINE_CASES = [
     # decode-like: one query row, D = 256, many splits
     dict(name="decode D256", seed=903, dtype="bf16", B=3, Sq=1, Sk=2000, Hq=8, Hkv=1, D=256, Dv=256,
          causal=True, splits=9, full_rows=True),
+    # at least 8192 (row, head) items and at most 64 splits: the wave-per-row merge
+    dict(name="many rows dense Dv96", seed=904, dtype="bf16", B=2, Sq=1100, Sk=1000, Hq=4, Hkv=2, D=128,
+         Dv=96, causal=True, splits=2),
+    dict(name="many rows varlen fp16", seed=905, dtype="fp16", B=0, Sq=0, Sk=0, Hq=2, Hkv=1, D=64, Dv=64,
+         causal=False, splits=3, lens=([3000, 0, 2500, 7], [300, 5, 0, 900])),
+    # pack-GQA D256 with seqused_k: every row of batch 0 is empty
+    dict(name="many rows D256 seqused", seed=906, dtype="bf16", B=2, Sq=600, Sk=1200, Hq=8, Hkv=1, D=256,
+         Dv=256, causal=False, splits=5, seqused=[0, 1100], pack_gqa=1),
+    dict(name="many rows D16 64 splits", seed=907, dtype="fp16", B=1, Sq=2100, Sk=8192, Hq=4, Hkv=4, D=16,
+         Dv=16, causal=True, splits=64, full_rows=True),
 ]
 
 
@@ -71,7 +82,7 @@ COMBINE_CASES = [
 def test_standalone_combine(cfg):
     c = random_case(cfg["seed"], dtype=cfg["dtype"], B=cfg["B"], Sq=cfg["Sq"], Sk=cfg["Sk"], Hq=cfg["Hq"],
                     Hkv=cfg["Hkv"], D=cfg["D"], Dv=cfg["Dv"], causal=cfg["causal"], varlen_lens=cfg.get("lens"),
-                    name="combine " + cfg["name"])
+                    seqused=cfg.get("seqused"), pack_gqa=cfg.get("pack_gqa", -1), name="combine " + cfg["name"])
     q, k, v = _tensors(c)
     ns = _splits(c, cfg["splits"])
     assert ns == cfg["splits"], ns
