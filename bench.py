@@ -464,10 +464,10 @@ class Run:
     """One workload's inputs resident in HBM, its preallocated outputs, and its timings."""
 
 
-def time_workload(workload, dtype, steps, warmup, warmup_seconds, copy_calibration=False):
+def time_workload(workload, dtype, steps, warmup, warmup_seconds, copy_calibration=False, num_splits=None):
     """Generate the workload's synthetic inputs, copy them to the GPU, warm up, then time
     exactly `steps` calls (wall clock around all of them, HIP events around each one on
-    the launch stream)."""
+    the launch stream). `num_splits`, when given, replaces the workload's split request."""
     import torch
 
     import exact_attention_forward_amd as fa
@@ -475,6 +475,8 @@ def time_workload(workload, dtype, steps, warmup, warmup_seconds, copy_calibrati
 
     r = Run()
     spec = configs.workload(workload, dtype)
+    if num_splits is not None:
+        spec.num_splits = num_splits
     log(f"generating {workload} ({DESCRIPTION[workload]}) {spec.dtype}")
     x = configs.make_inputs(spec)
     tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[spec.dtype]
@@ -641,6 +643,8 @@ def main():
                          "longer than a few steps of a sub-millisecond call")
     ap.add_argument("--workload", default="c2", choices=sorted(DESCRIPTION))
     ap.add_argument("--dtype", default=None, choices=["bf16", "fp16"])
+    ap.add_argument("--num-splits", type=int, default=None,
+                    help="replace the workload's split request (0 = the heuristic); traffic is then null")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
@@ -686,7 +690,7 @@ def main():
         sys.exit(2)
     fa.load()
     r = time_workload(args.workload, args.dtype, args.steps, args.warmup, args.warmup_seconds,
-                      args.copy_calibration)
+                      args.copy_calibration, args.num_splits)
     spec, x, q, k, v, kw, out, lse = r.spec, r.x, r.q, r.k, r.v, r.kw, r.out, r.lse
     varlen, ns, n_warm, ms_step, mean_call_ms = r.varlen, r.ns, r.n_warm, r.ms_step, r.mean_call_ms
 
@@ -708,7 +712,8 @@ def main():
         achieved = flops / (mean_call_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_MFMA_TFLOPS}
-    roof["traffic"] = read_traffic(args.workload, spec.dtype)
+    # the counters behind the traffic figure were taken at the workload's own split request
+    roof["traffic"] = read_traffic(args.workload, spec.dtype) if args.num_splits is None else None
     roof["kernel_ms"] = mean_call_ms
     roof["kernels_per_launch"] = 2 if ns > 1 else 1
     log(f"{args.workload}: {ms_step:.4f} ms/step wall, {mean_call_ms:.4f} ms/call events, "
