@@ -60,3 +60,13 @@ def test_report_covers_every_forward_instance():
     # 256 also has the decode form with the O columns split over the waves (64); the three
     # narrowed sets (96, 48, 192 columns) 32 each
     assert len(fwd) == 3 * 32 + 64 + 3 * 32, len(fwd)
+
+
+def test_combine_kernels_spill_nothing():
+    """Both split-KV merges (a work-group per row, a wave per row), every class and dtype."""
+    res = _load()
+    names = [n for n in res if re.search(r"attn_combine(_rows)?_kernel", n)]
+    assert len(names) == 2 * 4 * 2, names  # two kernels x classes 16/64/128/256 x bf16/fp16
+    for n in names:
+        assert int(res[n]["SGPRs Spill"]) == 0, n
+        assert int(res[n]["VGPRs Spill"]) == 0, n
