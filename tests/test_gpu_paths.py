@@ -242,6 +242,10 @@ GUARD_CASES = [
     dict(name="decode D256", seed=933, dtype="bf16", B=4, Sq=1, Sk=3000, Hq=8, Hkv=1, D=256, causal=True, splits=0),
     dict(name="Dv below class", seed=934, dtype="bf16", B=1, Sq=129, Sk=200, Hq=2, Hkv=2, D=128, Dv=72,
          causal=False, splits=3),
+    # the wave-per-row merge (>= 8192 items, <= 64 splits), 10198 items: the last work-group
+    # holds two items, so two of its waves have no row
+    dict(name="many rows merge", seed=935, dtype="fp16", B=0, Sq=0, Sk=0, Hq=2, Hkv=1, D=128, Dv=104,
+         causal=False, splits=3, lens=([4097, 0, 1002], [600, 77, 0])),
 ]
 
 
