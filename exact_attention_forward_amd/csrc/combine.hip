@@ -134,8 +134,8 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const CombineParams p
     if (p.lse && tid == 0) p.lse[lidx] = L;
 }
 
-// One wave per (query row, head), four per work-group, for calls with many rows and at
-// most 64 splits: lane s holds split s's LSE, so the max, the sum and the weights stay in
+// One wave per (query row, head), four per work-group, for calls with many rows, at most
+// 64 splits (use_rows_combine below): lane s holds split s's LSE, so the max, the sum and the weights stay in
 // registers (no LDS, no barrier), and the wave's lanes take 16-byte column chunks, SPW
 // splits side by side, U partial rows in flight per lane. The per-work-group fixed cost
 // of the kernel above (three barriers and an LDS round trip per row) is what bounds it
@@ -210,10 +210,19 @@ __global__ void __launch_bounds__(256) attn_combine_rows_kernel(const CombinePar
     if (p.lse && lane == 0) p.lse[lidx] = L;
 }
 
-// Calls with at least this many (row, head) items and at most 64 splits take the
-// wave-per-row kernel: enough waves to fill the chip several times over, so the merge is
-// bound by its reads, not by a work-group's fixed cost.
+// Calls with at most 64 splits take the wave-per-row kernel when they have at least
+// kRowsCombineMinItems (row, head) items (enough waves to fill the chip several times over,
+// so the merge is bound by its reads, not by a work-group's fixed cost), or at least
+// kRowsCombineFewItems items whose lanes each read at most two rounds of partial rows
+// (ns * Dv / 256 <= 2 * 8 chunks: the short-query split calls, 64 splits at Dv 64).
 constexpr long long kRowsCombineMinItems = 8192;
+constexpr long long kRowsCombineFewItems = 2048;
+
+inline bool use_rows_combine(const CombineParams& p, long long items) {
+    if (p.ns > 64) return false;
+    if (items >= kRowsCombineMinItems) return true;
+    return items >= kRowsCombineFewItems && (long long)p.ns * p.Dv <= 16 * 256;
+}
 
 template <int DV, bool BF>
 hipError_t launch_combine_t(const CombineParams& p, hipStream_t s) {
@@ -221,7 +230,7 @@ hipError_t launch_combine_t(const CombineParams& p, hipStream_t s) {
     if (items <= 0) return hipSuccess;
     CombineParams pp = p;
     void* args[] = {(void*)&pp};
-    if (p.ns <= 64 && items >= kRowsCombineMinItems) {
+    if (use_rows_combine(p, items)) {
         const long long blocks = (items + 3) / 4;  // four waves, four items per work-group
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
         return hipLaunchKernel((const void*)attn_combine_rows_kernel<DV, BF>, dim3((unsigned)blocks), dim3(256),
