@@ -213,15 +213,17 @@ __global__ void __launch_bounds__(256) attn_combine_rows_kernel(const CombinePar
 // Calls with at most 64 splits take the wave-per-row kernel when they have at least
 // kRowsCombineMinItems (row, head) items (enough waves to fill the chip several times over,
 // so the merge is bound by its reads, not by a work-group's fixed cost), or at least
-// kRowsCombineFewItems items whose lanes each read at most two rounds of partial rows
-// (ns * Dv / 256 <= 2 * 8 chunks: the short-query split calls, 64 splits at Dv 64).
+// kRowsCombineFewItems items whose lanes each read at most two rounds of U partial rows:
+// a lane of the class-DV kernel reads ns / (256 / DV) of them, so ns * DV <= 2 * 8 * 256
+// (the short-query split calls: 64 splits at class 64).
 constexpr long long kRowsCombineMinItems = 8192;
 constexpr long long kRowsCombineFewItems = 2048;
 
-inline bool use_rows_combine(const CombineParams& p, long long items) {
+template <int DV>
+bool use_rows_combine(const CombineParams& p, long long items) {
     if (p.ns > 64) return false;
     if (items >= kRowsCombineMinItems) return true;
-    return items >= kRowsCombineFewItems && (long long)p.ns * p.Dv <= 16 * 256;
+    return items >= kRowsCombineFewItems && (long long)p.ns * DV <= 16 * 256;
 }
 
 template <int DV, bool BF>
@@ -230,7 +232,7 @@ hipError_t launch_combine_t(const CombineParams& p, hipStream_t s) {
     if (items <= 0) return hipSuccess;
     CombineParams pp = p;
     void* args[] = {(void*)&pp};
-    if (use_rows_combine(p, items)) {
+    if (use_rows_combine<DV>(p, items)) {
         const long long blocks = (items + 3) / 4;  // four waves, four items per work-group
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
         return hipLaunchKernel((const void*)attn_combine_rows_kernel<DV, BF>, dim3((unsigned)blocks), dim3(256),

@@ -75,7 +75,7 @@ COMBINE_CASES = [
          Dv=256, causal=False, splits=5, seqused=[0, 1100], pack_gqa=1),
     dict(name="many rows D16 64 splits", seed=907, dtype="fp16", B=1, Sq=2100, Sk=8192, Hq=4, Hkv=4, D=16,
          Dv=16, causal=True, splits=64, full_rows=True),
-    # 2048..8191 items with at most two rounds of partial reads per lane (splits * Dv <= 4096):
+    # 2048..8191 items with at most two rounds of partial reads per lane (splits * class <= 4096):
     # also the wave-per-row merge (the short-query split calls)
     dict(name="short query 48 splits", seed=908, dtype="fp16", B=1, Sq=300, Sk=6000, Hq=8, Hkv=1, D=64,
          Dv=64, causal=False, splits=48, full_rows=True, pack_gqa=1),
